@@ -1,0 +1,177 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) KV-cache format-conversion library.
+ *
+ * The operations are the five functions of the ExLlamaV2 cache extension as
+ * described on the page "Implementation: Turboderp org Exllamav2 Ext Cache"
+ * (sections Description, Signature, I/O Contract, Usage Examples):
+ * fp16 <-> 8-bit, fp16 -> 4/6-bit block quantization of K and V with
+ * per-block fp16 scales, its inverse, over contiguous or paged caches, and a
+ * host-side matching-prefix count.  Tensors become raw pointers plus one
+ * shape descriptor; the page's implicit "current stream" becomes an explicit
+ * HIP stream argument.
+ *
+ * Conventions shared by every device call
+ *   - All device pointers belong to the current HIP device and are owned by
+ *     the caller.  The library allocates nothing, keeps no state between
+ *     calls and writes outputs in place, touching only the rows the call
+ *     covers; every other byte of an output buffer is left as it was.
+ *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
+ *     the default stream).  A kernel fault surfaces at the caller's next
+ *     synchronisation with that stream.
+ *   - Every base pointer of a device buffer must be 16-byte aligned
+ *     (allocations from hipMalloc or torch satisfy this); int32 tables need
+ *     4-byte alignment.
+ *   - Return 0 on success or a negative KVQ_ERR_* code; nothing is printed
+ *     and no exception crosses the ABI.  Arguments are validated on the host
+ *     before any launch; on error nothing is enqueued.
+ *   - batch_size == 0 or width == 0 validates the arguments and returns 0
+ *     without launching.
+ *
+ * Layouts (row = one token: heads * head_dim elements, R below)
+ *   fp16 cache     [dim0, dim1, heads, head_dim]            uint16 (fp16 bits)
+ *   8-bit cache    [dim0, dim1, heads, head_dim]            uint8
+ *   codes          [dim0, dim1, heads, head_dim * wbits/8]  uint8
+ *   scales         [dim0, dim1, heads, head_dim / 32]       fp16
+ *   Contiguous mode: dim0 = batch capacity, dim1 = sequence capacity.
+ *   Paged mode:      dim0 = number of physical pages, dim1 = page_size.
+ *
+ * Numerics (the page fixes the operations, not the arithmetic; the
+ * readings below are the library's definition):
+ *   8-bit  byte = high byte of the fp16 pattern (e5m2, truncated toward 0);
+ *          back: fp16 pattern = byte << 8.
+ *   Q4/Q6  blocks of 32 consecutive elements along head_dim;
+ *          s16 = fp16_rne(fp32(absmax) / (2^(b-1) - 1));
+ *          q = 0 if s16 == 0, else clamp(round_half_even(x / s16),
+ *              -2^(b-1), 2^(b-1) - 1); stored u = q + 2^(b-1);
+ *          the codes of a row form one little-endian bit stream, code j at
+ *          bits [b*j, b*j + b)  (4-bit: 8 codes per uint32 word; 6-bit: 16
+ *          codes per 12 bytes).
+ *   dequant x' = fp16_rne((float)(u - 2^(b-1)) * (float)s16).
+ *   Inputs to the quantizer must be finite; scales given to the dequantizer
+ *   must be finite.  Results are bit-identical across calls and devices.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported entry points (the library is built with hidden visibility). */
+#if defined(__GNUC__) || defined(__clang__)
+#define KVQ_API __attribute__((visibility("default")))
+#else
+#define KVQ_API
+#endif
+
+#define KVQ_OK            0
+#define KVQ_ERR_NULL     -1  /* a required pointer is NULL, or a K/V triple is partial */
+#define KVQ_ERR_WBITS    -2  /* wbits is not 4 or 6 */
+#define KVQ_ERR_SHAPE    -3  /* heads/head_dim/dims not positive, head_dim % 32 (Q) or
+                                heads*head_dim % 8 (8-bit) not 0, paged page_size != dim1 */
+#define KVQ_ERR_RANGE    -4  /* negative size or offset, window past dim0/dim1,
+                                block_table_cols <= 0 in paged mode, elem_bytes not 4/8 */
+#define KVQ_ERR_ALIGN    -5  /* a device base pointer is not 16-byte aligned (int32 tables: 4) */
+#define KVQ_ERR_OVERLAP  -6  /* an output buffer overlaps another buffer of the call */
+#define KVQ_ERR_HIP      -7  /* the HIP runtime rejected the launch */
+
+/* Physical cache shape shared by all tensors of one call. */
+typedef struct kvq_shape {
+    int32_t dim0;       /* batch capacity (contiguous) or number of pages (paged) */
+    int32_t dim1;       /* sequence capacity (contiguous) or page_size (paged) */
+    int32_t heads;
+    int32_t head_dim;
+} kvq_shape;
+
+/*
+ * fp16 -> 8-bit over the contiguous window: rows (b, offset + t) for
+ * b < batch_size, t < width.  ExLlamaV2 cache page, Description of
+ * fp16_to_fp8 ("FP16 cache tensors to FP8 (unsigned 8-bit)", strided 4D
+ * layout with batch_size, offset, width for partial updates).
+ *   in_f16  device, fp16 [dim0, dim1, heads, head_dim], read
+ *   out_u8  device, uint8 of the same shape, written on the window only
+ * Requires heads * head_dim % 8 == 0, batch_size <= dim0,
+ * offset + width <= dim1.
+ */
+KVQ_API int kvq_fp16_to_fp8(const void* in_f16, void* out_u8, kvq_shape s,
+                    int batch_size, int offset, int width, void* hip_stream);
+
+/*
+ * 8-bit -> fp16, the inverse of kvq_fp16_to_fp8 over the same window.
+ * ExLlamaV2 cache page, Description of fp8_to_fp16 (same shape validation and
+ * strided access pattern).
+ *   in_u8    device, uint8 [dim0, dim1, heads, head_dim], read
+ *   out_f16  device, fp16 of the same shape, written on the window only
+ */
+KVQ_API int kvq_fp8_to_fp16(const void* in_u8, void* out_f16, kvq_shape s,
+                    int batch_size, int offset, int width, void* hip_stream);
+
+/*
+ * fp16 -> 4/6-bit codes and per-block fp16 scales for K and V in one launch.
+ * ExLlamaV2 cache page, Description of fp16_to_q_kv (paged mode when
+ * page_size > 0, using block_table and cache_seqlens; contiguous otherwise)
+ * and I/O Contract (k_scales / v_scales: per-block scale factors; wbits 4/6).
+ *   k_in, v_in          device, fp16 [dim0, dim1, heads, head_dim], read
+ *   k_out, v_out        device, uint8 codes [dim0, dim1, heads, head_dim*wbits/8]
+ *   k_scales, v_scales  device, fp16 [dim0, dim1, heads, head_dim/32], written
+ *   Either triple may be all NULL to skip that half (at least one present);
+ *   a partially NULL triple is KVQ_ERR_NULL.
+ *   page_size == 0 (contiguous): rows (b, offset + t), b < batch_size <= dim0,
+ *     t < width, offset + width <= dim1; cache_seqlens/block_table ignored.
+ *   page_size  > 0 (paged, page_size == dim1): sequence b's position
+ *     p = cache_seqlens[b] + offset + t lives in physical page
+ *     block_table[b * block_table_cols + p / page_size], slot p % page_size.
+ *     A row is skipped (not read, not written) when p < 0, when
+ *     p / page_size >= block_table_cols, or when the page is outside
+ *     [0, dim0).  cache_seqlens: device int32[batch_size]; block_table:
+ *     device int32[batch_size, block_table_cols].  Two (b, t) mapping to the
+ *     same physical row give an unspecified result.
+ */
+KVQ_API int kvq_fp16_to_q_kv(const void* k_in, void* k_out, void* k_scales,
+                     const void* v_in, void* v_out, void* v_scales,
+                     kvq_shape s, int batch_size, int offset, int width,
+                     int page_size, const int32_t* cache_seqlens,
+                     const int32_t* block_table, int block_table_cols,
+                     int wbits, void* hip_stream);
+
+/*
+ * 4/6-bit codes + fp16 scales -> fp16 for K and V in one launch, over the
+ * same rows as kvq_fp16_to_q_kv with the same arguments.  ExLlamaV2 cache
+ * page, Description of q_to_fp16_kv (same paged/contiguous dual path) and
+ * I/O Contract (writes dequantized FP16 values into k_out / v_out).
+ *   k_in, v_in          device, uint8 codes [dim0, dim1, heads, head_dim*wbits/8], read
+ *   k_out, v_out        device, fp16 [dim0, dim1, heads, head_dim], written
+ *   k_scales, v_scales  device, fp16 [dim0, dim1, heads, head_dim/32], read
+ */
+KVQ_API int kvq_q_to_fp16_kv(const void* k_in, void* k_out, const void* k_scales,
+                     const void* v_in, void* v_out, const void* v_scales,
+                     kvq_shape s, int batch_size, int offset, int width,
+                     int page_size, const int32_t* cache_seqlens,
+                     const int32_t* block_table, int block_table_cols,
+                     int wbits, void* hip_stream);
+
+/*
+ * Length of the matching prefix of two host arrays of elem_bytes-byte
+ * elements (4 or 8), at most min(max_a, len_a, len_b) (0 when that is
+ * negative).  ExLlamaV2 cache page, Description of count_match (CPU-side,
+ * compares in 64-bit chunks, returns the matching prefix length, used for
+ * prefix reuse in dynamic batching).  Counts elements of the given size.
+ * Synchronous, host memory, no alignment requirement.  Returns the count, or
+ * KVQ_ERR_NULL / KVQ_ERR_RANGE (negative lengths, elem_bytes not 4 or 8).
+ */
+KVQ_API int64_t kvq_count_match(const void* a, int64_t len_a, const void* b, int64_t len_b,
+                        int64_t max_a, int elem_bytes);
+
+/* Static description of a KVQ_* code ("unknown error" for anything else). */
+KVQ_API const char* kvq_strerror(int code);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+KVQ_API int kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

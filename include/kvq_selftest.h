@@ -1,0 +1,52 @@
+/*
+ * kvq_selftest.h -- verification hooks of the kvq library.
+ *
+ * They run the exact device routines the conversion kernels use (scale rule,
+ * per-element code computation) on caller-chosen operands, so a test can
+ * sweep every fp16 (x, scale) pair against an independent reference.  The
+ * arithmetic they expose is the block quantization of the ExLlamaV2 cache
+ * page (Description of fp16_to_q_kv; I/O Contract: per-block scale factors,
+ * wbits 4 or 6) with the numeric reading stated in kvq.h.
+ * Same conventions as kvq.h: device pointers, asynchronous on hip_stream,
+ * 0 or a negative KVQ_ERR_* code.
+ */
+#ifndef KVQ_SELFTEST_H
+#define KVQ_SELFTEST_H
+
+#include <stdint.h>
+
+#include "kvq.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * u_out[i * nx + j] = offset-binary code (one per byte) of fp16 x[j] under
+ * the stored fp16 scale s16[i], for i < ns, j < nx.
+ *   x      device, fp16 bits [nx], nx % 8 == 0, 16-byte aligned
+ *   s16    device, fp16 bits [ns] (scales >= 0; 0 gives the zero code)
+ *   u_out  device, uint8 [ns, nx], 16-byte aligned
+ *   force_clamp  0: the kernels' own dispatch -- the clamp to
+ *                [-2^(b-1), 2^(b-1)-1] is applied only for subnormal scales,
+ *                which is exact whenever |x / s16| < 2^(b-1) - 1/2 (always
+ *                true for elements of the block a normal scale came from);
+ *                pairs outside that domain under a normal scale give an
+ *                unspecified code in this mode.
+ *                1: always take the clamping path (defined on every pair).
+ */
+KVQ_API int kvq_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s16, int64_t ns,
+                               int wbits, int force_clamp, uint8_t* u_out, void* hip_stream);
+
+/*
+ * out[i] = stored fp16 scale of a block whose absmax is the fp16 absmax[i]
+ * (>= 0, finite).  Device pointers, 2-byte aligned.
+ */
+KVQ_API int kvq_selftest_scales(const uint16_t* absmax, int64_t n, int wbits, uint16_t* out,
+                        void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_SELFTEST_H */

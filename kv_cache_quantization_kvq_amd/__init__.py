@@ -1,0 +1,290 @@
+"""kvq -- KV-cache format conversion on MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in include/kvq.h (libkvq.so, built in-tree
+by ``_build.build()``).  Each function has the name of its C entry point and
+only marshals arguments: dtype / shape / device checks on torch tensors,
+pointers, the current HIP stream.  Every step of the conversion runs in the
+HIP kernels; there is no fallback.  If the library has not been built, the
+first call raises.
+
+Operations (ExLlamaV2 cache page, Description / Signature / I/O Contract):
+  kvq_fp16_to_fp8 / kvq_fp8_to_fp16    fp16 <-> 8-bit (fp16 high byte)
+  kvq_fp16_to_q_kv / kvq_q_to_fp16_kv  fp16 <-> 4/6-bit block codes + fp16
+                                       scales, K and V in one launch,
+                                       contiguous or paged
+  kvq_count_match                      host matching-prefix length
+"""
+import ctypes
+import os
+
+from . import _build
+
+__all__ = ["KvqError", "kvq_fp16_to_fp8", "kvq_fp8_to_fp16", "kvq_fp16_to_q_kv",
+           "kvq_q_to_fp16_kv", "kvq_count_match", "kvq_strerror", "kvq_version",
+           "kvq_selftest_codes", "kvq_selftest_scales", "library_path", "load_library",
+           "code_shape", "scale_shape"]
+
+KVQ_OK = 0
+ERRORS = {-1: "KVQ_ERR_NULL", -2: "KVQ_ERR_WBITS", -3: "KVQ_ERR_SHAPE", -4: "KVQ_ERR_RANGE",
+          -5: "KVQ_ERR_ALIGN", -6: "KVQ_ERR_OVERLAP", -7: "KVQ_ERR_HIP"}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, code, fn):
+        self.code = code
+        super().__init__("%s failed: %s (%s)" % (fn, ERRORS.get(code, code), kvq_strerror(code)))
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("dim0", ctypes.c_int32), ("dim1", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+_LIB = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+
+
+def library_path():
+    return _build.LIB
+
+
+def load_library():
+    """Load libkvq.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(
+                "libkvq.so is not built (%s); run kv_cache_quantization_kvq_amd._build.build()"
+                % _build.LIB)
+        L = ctypes.CDLL(_build.LIB)
+        q_args = [_vp, _vp, _vp, _vp, _vp, _vp, Shape, _i, _i, _i, _i, _vp, _vp, _i, _i, _vp]
+        sig = {
+            "kvq_fp16_to_fp8": (_i, [_vp, _vp, Shape, _i, _i, _i, _vp]),
+            "kvq_fp8_to_fp16": (_i, [_vp, _vp, Shape, _i, _i, _i, _vp]),
+            "kvq_fp16_to_q_kv": (_i, q_args),
+            "kvq_q_to_fp16_kv": (_i, q_args),
+            "kvq_count_match": (_i64, [_vp, _i64, _vp, _i64, _i64, _i]),
+            "kvq_strerror": (ctypes.c_char_p, [_i]),
+            "kvq_version": (_i, []),
+            "kvq_selftest_codes": (_i, [_vp, _i64, _vp, _i64, _i, _i, _vp, _vp]),
+            "kvq_selftest_scales": (_i, [_vp, _i64, _i, _vp, _vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def kvq_strerror(code):
+    return load_library().kvq_strerror(int(code)).decode()
+
+
+def kvq_version():
+    return load_library().kvq_version()
+
+
+# ---------------------------------------------------------------- marshalling helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _check(rc, fn):
+    if rc != KVQ_OK:
+        raise KvqError(rc, fn)
+
+
+def _dev_ptr(t, name, dtype, device=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _table_ptr(t, name, device):
+    torch = _torch()
+    if t is None:
+        return None
+    return _dev_ptr(t, name, torch.int32, device)
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _expect_shape(t, shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def code_shape(cache_shape, wbits):
+    d0, d1, h, d = cache_shape
+    return (d0, d1, h, d * wbits // 8)
+
+
+def scale_shape(cache_shape):
+    d0, d1, h, d = cache_shape
+    return (d0, d1, h, d // 32)
+
+
+def _shape4(t, name):
+    if t.dim() != 4:
+        raise ValueError("%s must be 4-D [dim0, dim1, heads, head_dim]" % name)
+    return tuple(int(x) for x in t.shape)
+
+
+# ---------------------------------------------------------------- 8-bit
+def kvq_fp16_to_fp8(in_tensor, out_tensor, batch_size, offset, width, stream=None):
+    """fp16 cache -> uint8 cache (high byte), rows (b, offset + t) of the
+    window, b < batch_size, t < width.  Asynchronous on `stream`."""
+    torch = _torch()
+    shp = _shape4(in_tensor, "in_tensor")
+    dev = in_tensor.device
+    pi = _dev_ptr(in_tensor, "in_tensor", torch.float16)
+    po = _dev_ptr(out_tensor, "out_tensor", torch.uint8, dev)
+    _expect_shape(out_tensor, shp, "out_tensor")
+    rc = load_library().kvq_fp16_to_fp8(pi, po, Shape(*shp), int(batch_size), int(offset),
+                                        int(width), _stream_handle(stream, dev))
+    _check(rc, "kvq_fp16_to_fp8")
+
+
+def kvq_fp8_to_fp16(in_tensor, out_tensor, batch_size, offset, width, stream=None):
+    """uint8 cache -> fp16 cache (byte << 8) over the same window."""
+    torch = _torch()
+    shp = _shape4(in_tensor, "in_tensor")
+    dev = in_tensor.device
+    pi = _dev_ptr(in_tensor, "in_tensor", torch.uint8)
+    po = _dev_ptr(out_tensor, "out_tensor", torch.float16, dev)
+    _expect_shape(out_tensor, shp, "out_tensor")
+    rc = load_library().kvq_fp8_to_fp16(pi, po, Shape(*shp), int(batch_size), int(offset),
+                                        int(width), _stream_handle(stream, dev))
+    _check(rc, "kvq_fp8_to_fp16")
+
+
+# ---------------------------------------------------------------- 4/6-bit K/V
+def _q_common(quant, k_in, k_out, k_scales, v_in, v_out, v_scales, batch_size, offset, width,
+              page_size, cache_seqlens, block_table, wbits, stream):
+    torch = _torch()
+    fname = "kvq_fp16_to_q_kv" if quant else "kvq_q_to_fp16_kv"
+    f16 = k_in if quant else k_out
+    f16v = v_in if quant else v_out
+    ref = f16 if f16 is not None else f16v
+    if ref is None:
+        raise ValueError("%s: at least one of the K and V triples is required" % fname)
+    shp = _shape4(ref, "cache")
+    dev = ref.device
+    if wbits not in (4, 6):
+        raise ValueError("wbits must be 4 or 6")
+    cshape, sshape = code_shape(shp, wbits), scale_shape(shp)
+    src_t, dst_t = (torch.float16, torch.uint8) if quant else (torch.uint8, torch.float16)
+    src_s, dst_s = (shp, cshape) if quant else (cshape, shp)
+    ptrs = []
+    for nm, t, dt, sh in (("k_in", k_in, src_t, src_s), ("k_out", k_out, dst_t, dst_s),
+                          ("k_scales", k_scales, torch.float16, sshape),
+                          ("v_in", v_in, src_t, src_s), ("v_out", v_out, dst_t, dst_s),
+                          ("v_scales", v_scales, torch.float16, sshape)):
+        ptrs.append(_dev_ptr(t, nm, dt, dev))
+        _expect_shape(t, sh, nm)
+    cols = 0
+    psl = pbt = None
+    if page_size:
+        if cache_seqlens is None or block_table is None:
+            raise ValueError("paged mode needs cache_seqlens and block_table")
+        if block_table.dim() != 2 or block_table.shape[0] < batch_size:
+            raise ValueError("block_table must be [>= batch_size, cols]")
+        if cache_seqlens.dim() != 1 or cache_seqlens.shape[0] < batch_size:
+            raise ValueError("cache_seqlens must be [>= batch_size]")
+        cols = int(block_table.shape[1])
+        psl = _table_ptr(cache_seqlens, "cache_seqlens", dev)
+        pbt = _table_ptr(block_table, "block_table", dev)
+    fn = getattr(load_library(), fname)
+    rc = fn(*ptrs, Shape(*shp), int(batch_size), int(offset), int(width), int(page_size),
+            psl, pbt, cols, int(wbits), _stream_handle(stream, dev))
+    _check(rc, fname)
+
+
+def kvq_fp16_to_q_kv(k_in, k_out, k_scales, v_in, v_out, v_scales, batch_size, offset, width,
+                     page_size=0, cache_seqlens=None, block_table=None, wbits=4, stream=None):
+    """fp16 K/V caches -> codes [dim0, dim1, heads, head_dim*wbits/8] (uint8)
+    and scales [dim0, dim1, heads, head_dim/32] (fp16).  Pass None for a
+    whole triple to skip that half.  page_size > 0 selects the paged layout
+    (then cache_seqlens: int32[batch], block_table: int32[batch, cols])."""
+    _q_common(True, k_in, k_out, k_scales, v_in, v_out, v_scales, batch_size, offset, width,
+              page_size, cache_seqlens, block_table, wbits, stream)
+
+
+def kvq_q_to_fp16_kv(k_in, k_out, k_scales, v_in, v_out, v_scales, batch_size, offset, width,
+                     page_size=0, cache_seqlens=None, block_table=None, wbits=4, stream=None):
+    """codes + scales -> fp16 K/V caches over the same rows (k_in/v_in are the
+    codes, k_out/v_out the fp16 caches)."""
+    _q_common(False, k_in, k_out, k_scales, v_in, v_out, v_scales, batch_size, offset, width,
+              page_size, cache_seqlens, block_table, wbits, stream)
+
+
+# ---------------------------------------------------------------- host prefix compare
+def kvq_count_match(a, b, max_a):
+    """Length of the matching prefix of two 1-D host tensors / arrays of
+    4- or 8-byte integers, at most max_a."""
+    import numpy as np
+
+    def host(x, name):
+        if hasattr(x, "detach"):
+            if x.device.type != "cpu":
+                raise ValueError("%s must be in host memory" % name)
+            x = x.detach().contiguous().numpy()
+        x = np.ascontiguousarray(x)
+        if x.ndim != 1:
+            raise ValueError("%s must be 1-D" % name)
+        return x
+
+    a, b = host(a, "a"), host(b, "b")
+    if a.dtype != b.dtype or a.itemsize not in (4, 8):
+        raise TypeError("a and b must share a 4- or 8-byte integer dtype")
+    rc = load_library().kvq_count_match(a.ctypes.data, a.size, b.ctypes.data, b.size,
+                                        int(max_a), a.itemsize)
+    if rc < 0:
+        raise KvqError(int(rc), "kvq_count_match")
+    return int(rc)
+
+
+# ---------------------------------------------------------------- self-test hooks
+def kvq_selftest_codes(x_bits, s_bits, wbits, out, force_clamp=False, stream=None):
+    """out[i, j] = code of fp16 x_bits[j] under stored scale s_bits[i] (device
+    16-bit tensors, out uint8 [ns, nx]).  force_clamp=False uses the kernels'
+    own dispatch (defined for |x / s| < 2^(b-1) - 1/2 under normal scales)."""
+    torch = _torch()
+    dev = x_bits.device
+    px = _dev_ptr(x_bits.view(torch.int16), "x", torch.int16)
+    ps = _dev_ptr(s_bits.view(torch.int16), "s", torch.int16, dev)
+    po = _dev_ptr(out, "out", torch.uint8, dev)
+    _expect_shape(out, (s_bits.numel(), x_bits.numel()), "out")
+    rc = load_library().kvq_selftest_codes(px, x_bits.numel(), ps, s_bits.numel(), int(wbits),
+                                           int(bool(force_clamp)), po, _stream_handle(stream, dev))
+    _check(rc, "kvq_selftest_codes")
+
+
+def kvq_selftest_scales(a_bits, wbits, out, stream=None):
+    torch = _torch()
+    dev = a_bits.device
+    pa = _dev_ptr(a_bits.view(torch.int16), "absmax", torch.int16)
+    po = _dev_ptr(out.view(torch.int16), "out", torch.int16, dev)
+    rc = load_library().kvq_selftest_scales(pa, a_bits.numel(), int(wbits), po,
+                                            _stream_handle(stream, dev))
+    _check(rc, "kvq_selftest_scales")

@@ -1,0 +1,245 @@
+// kvq_api.cpp -- the C ABI declared in include/kvq.h: argument validation,
+// dispatch to the HIP launchers, and the host-side count_match.
+//
+// Operations and arguments: ExLlamaV2 cache page, Signature and I/O Contract
+// (batch_size, offset, width, page_size, cache_seqlens, block_table, wbits;
+// dtype checks kHalf <-> kUInt8).  Validation happens entirely on the host,
+// before anything is enqueued.
+#include <stdint.h>
+#include <string.h>
+
+#include <climits>
+
+#include "../../include/kvq.h"
+#include "../../include/kvq_selftest.h"
+#include "kvq_internal.h"
+
+namespace {
+
+using kvq::Fp8Launch;
+using kvq::QLaunch;
+
+constexpr int64_t kMaxRowElems = 1 << 20;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Extent {
+    const void* p;
+    int64_t bytes;
+    bool is_output;
+};
+
+bool overlaps(const Extent& x, const Extent& y) {
+    if (!x.p || !y.p || x.bytes <= 0 || y.bytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(x.p), a1 = a0 + (uintptr_t)x.bytes;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(y.p), b1 = b0 + (uintptr_t)y.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+// Any output extent overlapping any other extent of the call.
+bool any_output_overlap(const Extent* e, int n) {
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if ((e[i].is_output || e[j].is_output) && overlaps(e[i], e[j])) return true;
+    return false;
+}
+
+// Common shape/window checks.  `row_multiple` is the divisibility asked of
+// head_dim (Q paths) or of the row length (8-bit path).
+int check_shape(const kvq_shape& s, bool q_path) {
+    if (s.dim0 <= 0 || s.dim1 <= 0 || s.heads <= 0 || s.head_dim <= 0) return KVQ_ERR_SHAPE;
+    const int64_t R = (int64_t)s.heads * s.head_dim;
+    if (R > kMaxRowElems) return KVQ_ERR_SHAPE;
+    if (q_path ? (s.head_dim % 32 != 0) : (R % 8 != 0)) return KVQ_ERR_SHAPE;
+    return KVQ_OK;
+}
+
+int check_contig_window(const kvq_shape& s, int batch_size, int offset, int width) {
+    if (batch_size < 0 || offset < 0 || width < 0) return KVQ_ERR_RANGE;
+    if (batch_size > s.dim0) return KVQ_ERR_RANGE;
+    if ((int64_t)offset + width > s.dim1) return KVQ_ERR_RANGE;
+    return KVQ_OK;
+}
+
+int fp8_call(bool to_fp8, const void* in, void* out, kvq_shape s, int batch_size, int offset,
+             int width, void* stream) {
+    if (!in || !out) return KVQ_ERR_NULL;
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    rc = check_contig_window(s, batch_size, offset, width);
+    if (rc) return rc;
+    if (!aligned(in, 16) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
+    const int64_t R = (int64_t)s.heads * s.head_dim;
+    const int64_t elems = (int64_t)s.dim0 * s.dim1 * R;
+    const Extent ext[2] = {{in, elems * (to_fp8 ? 2 : 1), false}, {out, elems * (to_fp8 ? 1 : 2), true}};
+    if (any_output_overlap(ext, 2)) return KVQ_ERR_OVERLAP;
+    if ((int64_t)width * R / 8 / 1024 >= INT32_MAX) return KVQ_ERR_RANGE;   // grid.x bound
+    if (batch_size == 0 || width == 0) return KVQ_OK;
+    Fp8Launch a;
+    a.in = in;
+    a.out = out;
+    a.batch_stride_elems = (int64_t)s.dim1 * R;
+    a.first_elem = (int64_t)offset * R;
+    a.span_elems = (int64_t)width * R;
+    a.batch = batch_size;
+    const int err = to_fp8 ? kvq::launch_fp16_to_fp8(a, stream) : kvq::launch_fp8_to_fp16(a, stream);
+    return err ? KVQ_ERR_HIP : KVQ_OK;
+}
+
+int q_call(bool quant, const void* k_src, void* k_dst, const void* k_scales, const void* v_src,
+           void* v_dst, const void* v_scales, kvq_shape s, int batch_size, int offset, int width,
+           int page_size, const int32_t* cache_seqlens, const int32_t* block_table,
+           int block_table_cols, int wbits, void* stream) {
+    if (wbits != 4 && wbits != 6) return KVQ_ERR_WBITS;
+    const bool k_any = k_src || k_dst || k_scales, k_all = k_src && k_dst && k_scales;
+    const bool v_any = v_src || v_dst || v_scales, v_all = v_src && v_dst && v_scales;
+    if ((k_any && !k_all) || (v_any && !v_all) || (!k_any && !v_any)) return KVQ_ERR_NULL;
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    if (page_size < 0) return KVQ_ERR_RANGE;
+    if (page_size == 0) {
+        rc = check_contig_window(s, batch_size, offset, width);
+        if (rc) return rc;
+    } else {
+        if (page_size != s.dim1) return KVQ_ERR_SHAPE;
+        if (batch_size < 0 || offset < 0 || width < 0 || block_table_cols <= 0) return KVQ_ERR_RANGE;
+        if ((int64_t)block_table_cols * page_size > INT32_MAX) return KVQ_ERR_RANGE;
+        if (!cache_seqlens || !block_table) return KVQ_ERR_NULL;
+        if (!aligned(cache_seqlens, 4) || !aligned(block_table, 4)) return KVQ_ERR_ALIGN;
+    }
+    const int64_t R = (int64_t)s.heads * s.head_dim;
+    const int64_t nseg = (R / 8 + 127) / 128;
+    if ((int64_t)batch_size * width * nseg > INT32_MAX) return KVQ_ERR_RANGE;
+    const void* ptrs[6] = {k_src, k_dst, k_scales, v_src, v_dst, v_scales};
+    for (const void* p : ptrs)
+        if (p && !aligned(p, 16)) return KVQ_ERR_ALIGN;
+
+    const int64_t rows = (int64_t)s.dim0 * s.dim1;
+    const int64_t f16_bytes = rows * R * 2, code_bytes = rows * R / 8 * wbits, scale_bytes = rows * (R / 32) * 2;
+    const int64_t src_bytes = quant ? f16_bytes : code_bytes, dst_bytes = quant ? code_bytes : f16_bytes;
+    const Extent ext[8] = {
+        {k_src, src_bytes, false}, {k_dst, dst_bytes, true}, {k_scales, scale_bytes, quant},
+        {v_src, src_bytes, false}, {v_dst, dst_bytes, true}, {v_scales, scale_bytes, quant},
+        {cache_seqlens, page_size ? (int64_t)batch_size * 4 : 0, false},
+        {block_table, page_size ? (int64_t)batch_size * block_table_cols * 4 : 0, false}};
+    if (any_output_overlap(ext, 8)) return KVQ_ERR_OVERLAP;
+    if (batch_size == 0 || width == 0) return KVQ_OK;
+
+    QLaunch a;
+    a.k_src = k_src; a.k_dst = k_dst; a.k_scales = const_cast<void*>(k_scales);
+    a.v_src = v_src; a.v_dst = v_dst; a.v_scales = const_cast<void*>(v_scales);
+    a.dim0 = s.dim0; a.dim1 = s.dim1; a.R = (int32_t)R;
+    a.batch = batch_size; a.offset = offset; a.width = width;
+    a.page_size = page_size;
+    a.cache_seqlens = page_size ? cache_seqlens : nullptr;
+    a.block_table = page_size ? block_table : nullptr;
+    a.bt_cols = page_size ? block_table_cols : 0;
+    a.wbits = wbits;
+    const int err = quant ? kvq::launch_quant_kv(a, stream) : kvq::launch_dequant_kv(a, stream);
+    return err ? KVQ_ERR_HIP : KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_fp16_to_fp8(const void* in_f16, void* out_u8, kvq_shape s, int batch_size, int offset,
+                    int width, void* hip_stream) {
+    return fp8_call(true, in_f16, out_u8, s, batch_size, offset, width, hip_stream);
+}
+
+int kvq_fp8_to_fp16(const void* in_u8, void* out_f16, kvq_shape s, int batch_size, int offset,
+                    int width, void* hip_stream) {
+    return fp8_call(false, in_u8, out_f16, s, batch_size, offset, width, hip_stream);
+}
+
+int kvq_fp16_to_q_kv(const void* k_in, void* k_out, void* k_scales, const void* v_in, void* v_out,
+                     void* v_scales, kvq_shape s, int batch_size, int offset, int width,
+                     int page_size, const int32_t* cache_seqlens, const int32_t* block_table,
+                     int block_table_cols, int wbits, void* hip_stream) {
+    return q_call(true, k_in, k_out, k_scales, v_in, v_out, v_scales, s, batch_size, offset, width,
+                  page_size, cache_seqlens, block_table, block_table_cols, wbits, hip_stream);
+}
+
+int kvq_q_to_fp16_kv(const void* k_in, void* k_out, const void* k_scales, const void* v_in,
+                     void* v_out, const void* v_scales, kvq_shape s, int batch_size, int offset,
+                     int width, int page_size, const int32_t* cache_seqlens,
+                     const int32_t* block_table, int block_table_cols, int wbits,
+                     void* hip_stream) {
+    return q_call(false, k_in, k_out, k_scales, v_in, v_out, v_scales, s, batch_size, offset, width,
+                  page_size, cache_seqlens, block_table, block_table_cols, wbits, hip_stream);
+}
+
+// Matching prefix in 64-bit chunks (ExLlamaV2 cache page, Description of
+// count_match): whole 8-byte words are compared four at a time, the first
+// differing word is then resolved element by element.
+int64_t kvq_count_match(const void* a, int64_t len_a, const void* b, int64_t len_b, int64_t max_a,
+                        int elem_bytes) {
+    if (elem_bytes != 4 && elem_bytes != 8) return KVQ_ERR_RANGE;
+    if (len_a < 0 || len_b < 0) return KVQ_ERR_RANGE;
+    int64_t n = max_a < len_a ? max_a : len_a;
+    if (len_b < n) n = len_b;
+    if (n <= 0) return 0;
+    if (!a || !b) return KVQ_ERR_NULL;
+    const unsigned char* pa = static_cast<const unsigned char*>(a);
+    const unsigned char* pb = static_cast<const unsigned char*>(b);
+    const int64_t nbytes = n * elem_bytes;
+    const int64_t nwords = nbytes / 8;
+    int64_t w = 0;
+    for (; w + 4 <= nwords; w += 4) {
+        uint64_t x[4], y[4];
+        memcpy(x, pa + 8 * w, 32);
+        memcpy(y, pb + 8 * w, 32);
+        if (((x[0] ^ y[0]) | (x[1] ^ y[1]) | (x[2] ^ y[2]) | (x[3] ^ y[3])) != 0) break;
+    }
+    for (; w < nwords; ++w) {
+        uint64_t x, y;
+        memcpy(&x, pa + 8 * w, 8);
+        memcpy(&y, pb + 8 * w, 8);
+        if (x != y) break;
+    }
+    // first element not covered by equal words
+    int64_t i = (8 * w) / elem_bytes;
+    for (; i < n; ++i)
+        if (memcmp(pa + i * elem_bytes, pb + i * elem_bytes, (size_t)elem_bytes) != 0) return i;
+    return n;
+}
+
+const char* kvq_strerror(int code) {
+    switch (code) {
+        case KVQ_OK: return "success";
+        case KVQ_ERR_NULL: return "required pointer is NULL or a K/V triple is partial";
+        case KVQ_ERR_WBITS: return "wbits must be 4 or 6";
+        case KVQ_ERR_SHAPE: return "invalid cache shape (head_dim % 32 for Q paths, heads*head_dim % 8 for 8-bit, page_size == dim1 when paged)";
+        case KVQ_ERR_RANGE: return "size, offset or window out of range";
+        case KVQ_ERR_ALIGN: return "device pointer not 16-byte aligned (int32 tables: 4)";
+        case KVQ_ERR_OVERLAP: return "an output buffer overlaps another buffer of the call";
+        case KVQ_ERR_HIP: return "HIP launch failed";
+        default: return "unknown error";
+    }
+}
+
+int kvq_version(void) { return 100; }
+
+int kvq_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s16, int64_t ns, int wbits,
+                       int force_clamp, uint8_t* u_out, void* hip_stream) {
+    if (wbits != 4 && wbits != 6) return KVQ_ERR_WBITS;
+    if (!x || !s16 || !u_out) return KVQ_ERR_NULL;
+    if (nx < 0 || ns < 0 || nx % 8 != 0) return KVQ_ERR_RANGE;
+    if (!aligned(x, 16) || !aligned(u_out, 16) || !aligned(s16, 2)) return KVQ_ERR_ALIGN;
+    if (nx == 0 || ns == 0) return KVQ_OK;
+    if ((nx / 8) * ns > (int64_t)INT32_MAX * 64) return KVQ_ERR_RANGE;
+    return kvq::launch_selftest_codes(x, nx, s16, ns, wbits, force_clamp != 0, u_out, hip_stream)
+               ? KVQ_ERR_HIP : KVQ_OK;
+}
+
+int kvq_selftest_scales(const uint16_t* absmax, int64_t n, int wbits, uint16_t* out, void* hip_stream) {
+    if (wbits != 4 && wbits != 6) return KVQ_ERR_WBITS;
+    if (!absmax || !out) return KVQ_ERR_NULL;
+    if (n < 0 || n > (int64_t)INT32_MAX * 64) return KVQ_ERR_RANGE;
+    if (!aligned(absmax, 2) || !aligned(out, 2)) return KVQ_ERR_ALIGN;
+    if (n == 0) return KVQ_OK;
+    return kvq::launch_selftest_scales(absmax, n, wbits, out, hip_stream) ? KVQ_ERR_HIP : KVQ_OK;
+}
+
+}  // extern "C"

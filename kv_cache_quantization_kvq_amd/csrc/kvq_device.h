@@ -1,0 +1,221 @@
+// kvq_device.h -- gfx950 device building blocks of the KV-cache conversions.
+//
+// A "chunk" is 8 consecutive fp16 elements of a token row (one 128-bit
+// load).  Four consecutive lanes hold one 32-element quantization block, so
+// block reductions are DPP quad permutations inside a wave (no LDS).
+//
+// Arithmetic definitions (ExLlamaV2 cache page, Description of fp16_to_q_kv /
+// q_to_fp16_kv; the numeric reading is stated in kvq.h):
+//   scale  s16 = fp16_rne(absmax / Q),  Q = 2^(b-1) - 1
+//   code   q = clamp(round_half_even(x / s16), -Z, Z-1), Z = 2^(b-1); u = q + Z
+//   value  x' = fp16_rne(q * s16)
+// How each is computed here without a per-element IEEE divide is described
+// next to the function that does it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
+    return (float)h;
+}
+
+// fp32 -> fp16 bits, round to nearest even, subnormals kept (v_cvt_f16_f32
+// under the default MODE: round-nearest-even, fp16 denormals enabled).
+__device__ __forceinline__ uint32_t f2h(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+__device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// ---------------------------------------------------------------- reductions
+
+// Largest |x| of the 8 fp16 values of a chunk, as fp16 bits.  For finite
+// values, ordering of |x| equals unsigned ordering of the bits with the sign
+// cleared, so this is packed u16 max on (bits & 0x7FFF).
+__device__ __forceinline__ uint32_t absmax_chunk(uint4 v) {
+    u16x2_t a = __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu);
+    u16x2_t b = __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu);
+    u16x2_t c = __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu);
+    u16x2_t d = __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu);
+    u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                          __builtin_elementwise_max(c, d));
+    return (uint32_t)(m.x > m.y ? m.x : m.y);
+}
+
+// DPP quad_perm controls: [1,0,3,2] and [2,3,0,1].
+constexpr int kQuadSwap1 = 0xB1;
+constexpr int kQuadSwap2 = 0x4E;
+
+// Max over the 4 lanes of a quad (all four lanes of a quad are always
+// active together: a block never straddles a quad).
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+    uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false);
+    v = v > o ? v : o;
+    o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap2, 0xF, 0xF, false);
+    return v > o ? v : o;
+}
+
+// Value of the partner lane (lane ^ 1).
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false);
+}
+
+// ---------------------------------------------------------------- scale
+
+// s16 = fp16_rne(a / Q) computed as fp16_rne(a * fl32(1/Q)).  For every
+// finite fp16 a and Q in {7, 31} this equals the correctly rounded a/Q: the
+// product is within 1.5 ulp32 of a/Q, and a/Q is never that close to an
+// fp16 rounding boundary unless it is exactly representable (checked
+// exhaustively on the device by the self-test hooks).
+template <int WBITS>
+__device__ __forceinline__ uint32_t scale_from_absmax(uint32_t a_bits) {
+    constexpr float kInvQ = 1.0f / (float)((1 << (WBITS - 1)) - 1);
+    return f2h(h2f(a_bits) * kInvQ);
+}
+
+// ---------------------------------------------------------------- quantize
+
+// y = x * r with x one fp16 half of a word (low or high), r fp32, in one
+// v_fma_mix_f32 (the f16 operand is widened exactly inside the instruction;
+// the +0 addend only affects the sign of a zero product, which no code
+// depends on).
+__device__ __forceinline__ float mul_f16lo(uint32_t w, float r) {
+    float y;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(y) : "v"(w), "v"(r));
+    return y;
+}
+__device__ __forceinline__ float mul_f16hi(uint32_t w, float r) {
+    float y;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(y) : "v"(w), "v"(r));
+    return y;
+}
+
+// Code of one element; the low WBITS bits of the result are u = q + Z, the
+// bits from 24 up hold the exponent of the rounding constant (bits WBITS..23
+// are zero).
+//
+// q = round_half_even(x / s) is obtained without a divide:
+//   y  = x * r                r = rcp(s), within 1 ulp of 1/s
+//   e  = fma(-y, s, x)        exact residual x - y*s
+//   y2 = fma(e, r, y)         corrected quotient
+// For fp16 x and s, x/s is either an exact half-integer tie (then y2 lands
+// on it exactly, the correction being far below half an ulp) or lies at
+// least ~2^-13 relative from any tie, far beyond the few-ulp error of y2;
+// so rounding y2 gives round_half_even(x / s) on every pair.
+// Adding M = 2^23 + Z rounds to an integer with ties-to-even (the fp32 ulp
+// in [2^23, 2^24) is 1; Z is even, so parity is kept) and leaves u in the
+// low mantissa bits.
+// The clamp to [-Z, Z-1] (which commutes with rounding: integer bounds) can
+// only act when s is an fp16 subnormal: a normal s16 = fp16_rne(a / Q) is at
+// least (a / Q) * (1 - 2^-11), so every element of its block has
+// |x / s16| <= Q * (1 + 2^-10) < Q + 1/2, which keeps y2 + M inside
+// [2^23, 2^24) and the rounded code inside [-Q, Q].  Without the clamp the
+// routine is therefore only valid on that domain.
+template <int WBITS, bool CLAMP>
+__device__ __forceinline__ uint32_t quant_elem(float y, uint32_t w, bool hi, float s, float r) {
+    constexpr float Z = (float)(1 << (WBITS - 1));
+    constexpr float M = 8388608.0f + Z;
+    float e;
+    if (hi)
+        asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(e) : "v"(y), "v"(s), "v"(w));
+    else
+        asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel_hi:[0,0,1]" : "=v"(e) : "v"(y), "v"(s), "v"(w));
+    float y2 = __builtin_fmaf(e, r, y);
+    if (CLAMP) y2 = __builtin_amdgcn_fmed3f(y2, -Z, Z - 1.0f);
+    return __builtin_bit_cast(uint32_t, y2 + M);
+}
+
+// 8 codes of a chunk, code j in the low WBITS bits of u[j].
+template <int WBITS, bool CLAMP>
+__device__ __forceinline__ void quant_chunk_impl(uint4 v, float s, float r, uint32_t (&u)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        u[2 * i] = quant_elem<WBITS, CLAMP>(mul_f16lo(w[i], r), w[i], false, s, r);
+        u[2 * i + 1] = quant_elem<WBITS, CLAMP>(mul_f16hi(w[i], r), w[i], true, s, r);
+    }
+}
+
+// s16 is the block's stored scale (fp16 bits); (s, r) from prep_scale.
+template <int WBITS>
+__device__ __forceinline__ void quant_chunk(uint4 v, uint32_t s16, float s, float r, uint32_t (&u)[8]) {
+    if (s16 >= 0x0400u) quant_chunk_impl<WBITS, false>(v, s, r, u);
+    else quant_chunk_impl<WBITS, true>(v, s, r, u);
+}
+
+// 4-bit: code j at bits 4j..4j+3 of one little-endian word.  Codes 2..7
+// shift their high garbage past bit 31; codes 0 and 1 are merged through
+// their low byte.
+__device__ __forceinline__ uint32_t pack_q4(const uint32_t (&u)[8]) {
+    uint32_t w = u[2] << 8;
+#pragma unroll
+    for (int j = 3; j < 8; ++j) w |= u[j] << (4 * j);
+    const uint32_t t = u[0] | (u[1] << 4);
+    return (t & 0xFFu) | w;
+}
+
+// 6-bit: code j at bits 6j..6j+5 of a 48-bit little-endian field, returned
+// as (lo32, hi) where only the low 16 bits of hi are meaningful.
+__device__ __forceinline__ void pack_q6(const uint32_t (&u)[8], uint32_t& lo, uint32_t& hi) {
+    uint32_t w = (u[2] << 12) | (u[3] << 18) | (u[4] << 24) | (u[5] << 30);
+    const uint32_t t = u[0] | (u[1] << 6);
+    lo = (t & 0xFFFu) | w;
+    hi = (u[5] >> 2) | (u[6] << 4) | (u[7] << 10);
+}
+
+// ---------------------------------------------------------------- dequantize
+//
+// Codes become exact fp16 integers through the bit pattern 0x6400 | u
+// (= 1024 + u: the fp16 ulp in [1024, 2048) is 1), the offset is removed
+// with an exact packed fma, and q * s16 is one correctly rounded packed fp16
+// multiply (fp16 denormals enabled), i.e. exactly fp16_rne(q * s16).
+
+// Pair of 4-bit codes held in one byte (low nibble first) -> (q_lo, q_hi).
+// The byte is replicated into bytes 0 and 2; the low nibble stays at bits
+// 0..3 (value 1024 + u0) and the high nibble lands at bits 20..23 (value
+// 1024 + 16*u1), undone by the 1/16 factor.
+__device__ __forceinline__ half2_t q4_pair(uint32_t w, uint32_t sel) {
+    uint32_t t = __builtin_amdgcn_perm(w, w, sel);
+    t = (t & 0x00F0000Fu) | 0x64006400u;
+    const half2_t mul = {(_Float16)1.0f, (_Float16)0.0625f};
+    const half2_t add = {(_Float16)-1032.0f, (_Float16)-72.0f};
+    return __builtin_elementwise_fma(as_h2(t), mul, add);
+}
+
+__device__ __forceinline__ uint4 dequant_q4_chunk(uint32_t w, uint32_t s2) {
+    const half2_t s = as_h2(s2);
+    uint4 o;
+    o.x = as_u32(q4_pair(w, 0x00000000u) * s);
+    o.y = as_u32(q4_pair(w, 0x01010101u) * s);
+    o.z = as_u32(q4_pair(w, 0x02020202u) * s);
+    o.w = as_u32(q4_pair(w, 0x03030303u) * s);
+    return o;
+}
+
+// Pair of 6-bit codes at bits 0..11 of f -> (q_lo, q_hi).
+__device__ __forceinline__ half2_t q6_pair(uint32_t f) {
+    uint32_t t = (f & 0x0000FFFFu) | ((f << 10) & 0xFFFF0000u);
+    t = (t & 0x003F003Fu) | 0x64006400u;
+    const half2_t off = {(_Float16)-1056.0f, (_Float16)-1056.0f};
+    return as_h2(t) + off;
+}
+
+__device__ __forceinline__ uint4 dequant_q6_chunk(uint32_t lo, uint32_t hi, uint32_t s2) {
+    const half2_t s = as_h2(s2);
+    uint4 o;
+    o.x = as_u32(q6_pair(lo) * s);
+    o.y = as_u32(q6_pair(lo >> 12) * s);
+    o.z = as_u32(q6_pair(__builtin_amdgcn_alignbit(hi, lo, 24)) * s);
+    o.w = as_u32(q6_pair(hi >> 4) * s);
+    return o;
+}
+
+}  // namespace kvq

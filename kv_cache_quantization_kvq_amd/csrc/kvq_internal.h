@@ -1,0 +1,49 @@
+// kvq_internal.h -- launch descriptors shared by the host API and the HIP
+// launchers.  Plain C++ (no HIP types), so the validation layer stays
+// host-only code.
+#pragma once
+
+#include <stdint.h>
+
+namespace kvq {
+
+// One call of the fp16 <-> 8-bit conversion: `batch` spans of `span_elems`
+// contiguous elements; span b starts at element b * batch_stride_elems.
+struct Fp8Launch {
+    const void* in;
+    void* out;
+    int64_t batch_stride_elems;   // dim1 * R
+    int64_t first_elem;           // offset * R
+    int64_t span_elems;           // width * R (a multiple of 8)
+    int32_t batch;
+};
+
+// One call of the K/V block (de)quantization.  For quantization `k_src` /
+// `v_src` are fp16 caches and `k_dst` / `v_dst` code buffers; for
+// dequantization the roles swap.  Scales are written by quantization and read
+// by dequantization.  A NULL source skips that half.
+struct QLaunch {
+    const void* k_src; void* k_dst; void* k_scales;
+    const void* v_src; void* v_dst; void* v_scales;
+    int32_t dim0, dim1;           // physical shape (pages x page_size when paged)
+    int32_t R;                    // elements per token row (heads * head_dim, % 32 == 0)
+    int32_t batch, offset, width;
+    int32_t page_size;            // 0: contiguous
+    const int32_t* cache_seqlens; // paged only
+    const int32_t* block_table;   // paged only, [batch, bt_cols]
+    int32_t bt_cols;
+    int32_t wbits;
+};
+
+// Launchers (return a hipError_t value as int, 0 on success).
+int launch_fp16_to_fp8(const Fp8Launch& a, void* stream);
+int launch_fp8_to_fp16(const Fp8Launch& a, void* stream);
+int launch_quant_kv(const QLaunch& a, void* stream);
+int launch_dequant_kv(const QLaunch& a, void* stream);
+
+// Element-level self-test launchers (same device routines as the kernels).
+int launch_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s, int64_t ns,
+                          int wbits, bool force_clamp, uint8_t* u, void* stream);
+int launch_selftest_scales(const uint16_t* a, int64_t n, int wbits, uint16_t* out, void* stream);
+
+}  // namespace kvq

@@ -45,6 +45,20 @@ def test_scale_underflow_counts(wbits, n_zero, n_sub):
 
 
 # ---------------------------------------------------------------- codes
+@pytest.mark.parametrize("wbits", [4, 6])
+def test_normal_scale_never_needs_the_clamp(wbits):
+    """For every finite absmax a whose stored scale s16 is a normal fp16,
+    a / s16 < Q + 1/2 exactly: every element of such a block rounds into
+    [-Q, Q] without clamping (the clamp only acts under subnormal scales)."""
+    Q, _ = QZ(wbits)
+    s = oracle.scale_from_absmax(POS_FINITE, wbits)
+    normal = s >= 0x0400
+    A = f16_units(POS_FINITE[normal])
+    S = f16_units(s[normal])
+    assert (2 * A < (2 * Q + 1) * S).all()
+    assert normal.sum() > 20000
+
+
 def _scale_sample():
     """Every subnormal scale, every 16th normal scale, and all scales with an
     all-ones or all-zeros mantissa (binade edges)."""
