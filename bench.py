@@ -1,0 +1,415 @@
+#!/usr/bin/env python3
+"""Throughput of the paged Q4 KV-cache quantize + dequantize path on one GPU.
+
+Step = one pass of the hot path over one batch: fp16 K and V rows of 32
+sequences x 256 new tokens, resolved through block_table / cache_seqlens
+(4096 physical pages x 256 tokens, 8 heads x 128), quantized to 4-bit codes
++ fp16 scales (one launch for K and V), then dequantized back to fp16 (one
+launch).  The ExLlamaV2 cache page describes these operations
+(fp16_to_q_kv / q_to_fp16_kv, paged mode with page_size 256 in its usage
+example).
+
+Cold data: 32 seeded (cache_seqlens, block_table) draws are rotated, so each
+step touches rows the previous 31 steps did not (about 1.4 GB between reuses,
+beyond the 256 MB last-level cache).  The timed region replays HIP graphs of
+the steps (launch overhead off the host) between device synchronisations.
+
+Output: one JSON line (metric, value = algorithmic GB/s of the whole job,
+ms_per_step, roofline of the dominant kernel measured with HIP events,
+cpu_baseline = the CPU oracle on a bounded sample, timed on the host cores).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV quant+dequant GB/s (read+write) and % of HBM peak, paged Q4, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+DRAWS = 32
+HEADS, HEAD_DIM, PAGE = 8, 128, 256
+ROW = HEADS * HEAD_DIM
+
+
+def q_row_bytes(wbits):
+    """Algorithmic bytes per token row, either direction: fp16 row + codes + scales."""
+    return ROW * 2 + ROW * wbits // 8 + (ROW // 32) * 2
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=640)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    p.add_argument("--streams", type=int, default=2,
+                   help="independent step chains replayed concurrently (1 = strictly serial steps)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' kernel timings")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain device copy of known size (counter calibration)")
+    p.add_argument("--cpu-draws", type=int, default=16, help="draws in the CPU-oracle sample")
+    return p.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class PagedQ4:
+    """Device state of the paged Q4 workload and its two launches."""
+
+    def __init__(self, torch, kvq, synth):
+        self.torch, self.kvq = torch, kvq
+        w = synth.q4_paged(draws=DRAWS)
+        self.w = w
+        shape = w.shape
+        t = torch
+        log("allocating paged caches %s x 2 (fp16) + codes/scales/outputs" % (shape,))
+        self.k = synth.device_normal_f16(t, shape, w.extra["device_seed"])
+        self.v = synth.device_normal_f16(t, shape, w.extra["device_seed"] + 1)
+        cs, ss = kvq.code_shape(shape, 4), kvq.scale_shape(shape)
+        self.kq = t.zeros(cs, dtype=t.uint8, device="cuda")
+        self.vq = t.zeros(cs, dtype=t.uint8, device="cuda")
+        self.ks = t.zeros(ss, dtype=t.float16, device="cuda")
+        self.vs = t.zeros(ss, dtype=t.float16, device="cuda")
+        self.ko = t.zeros(shape, dtype=t.float16, device="cuda")
+        self.vo = t.zeros(shape, dtype=t.float16, device="cuda")
+        self.tables = [(t.from_numpy(sl).cuda(), t.from_numpy(bt).cuda()) for sl, bt in w.extra["tables"]]
+        self.rows_per_launch = 2 * w.batch_size * w.width            # K and V rows
+        self.bytes_per_launch = self.rows_per_launch * q_row_bytes(4)
+        self.bytes_per_step = 2 * self.bytes_per_launch
+        self.elems_per_step = 2 * self.rows_per_launch * ROW
+
+    def quant(self, d):
+        sl, bt = self.tables[d]
+        w = self.w
+        self.kvq.kvq_fp16_to_q_kv(self.k, self.kq, self.ks, self.v, self.vq, self.vs, w.batch_size,
+                                  w.offset, w.width, w.page_size, sl, bt, 4)
+
+    def dequant(self, d):
+        sl, bt = self.tables[d]
+        w = self.w
+        self.kvq.kvq_q_to_fp16_kv(self.kq, self.ko, self.ks, self.vq, self.vo, self.vs, w.batch_size,
+                                  w.offset, w.width, w.page_size, sl, bt, 4)
+
+    def step(self, d):
+        self.quant(d)
+        self.dequant(d)
+
+
+def time_kernels(torch, launches, reps):
+    """Average device duration of each named launch: `reps` launches of that
+    kernel alone (rotating over its argument list) are captured in one HIP
+    graph, which is replayed between two events on the current stream.
+    Consecutive launches in a graph run back to back, so the average is the
+    kernel's own duration plus the (near-zero) dispatch gap; returns
+    {name: seconds}."""
+    out = {}
+    for name, fn, args in launches:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(len(args)):
+                fn(args[i])
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                fn(args[i % len(args)])
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = a.elapsed_time(b) * 1e-3 / reps
+        del g
+    return out
+
+
+def cpu_baseline(wl, oracle, rows_fn, draws):
+    """The CPU oracle (plain scalar C) quantizing then dequantizing the same
+    rows as `draws` GPU steps, rows split over host threads.  Returns the
+    timing and, per (draw, tensor), the oracle's codes / scales / fp16 rows."""
+    from concurrent.futures import ThreadPoolExecutor
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    groups = []                                  # (draw, name, rows, host fp16 rows)
+    for d in range(draws):
+        sl, bt = wl.w.extra["tables"][d]
+        rows = oracle.call_rows(wl.w.shape[0], wl.w.shape[1], wl.w.batch_size, wl.w.offset,
+                                wl.w.width, wl.w.page_size, sl, bt)
+        rows = rows[rows >= 0]
+        groups.append((d, "K", rows, rows_fn(wl.k, rows)))
+        groups.append((d, "V", rows, rows_fn(wl.v, rows)))
+    jobs = [(g, chunk) for g in range(len(groups))
+            for chunk in np.array_split(np.arange(groups[g][3].shape[0]), threads)]
+
+    def work(job):
+        g, chunk = job
+        c, s = oracle.quant_rows(groups[g][3][chunk], 4)
+        return c, s, oracle.dequant_rows(c, s, 4)
+
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        t0 = time.perf_counter()
+        results = list(pool.map(work, jobs))
+        dt = time.perf_counter() - t0
+    per_group = []
+    for g, (d, name, rows, _) in enumerate(groups):
+        mine = [r for (gg, _), r in zip(jobs, results) if gg == g]
+        per_group.append((d, name, rows, *(np.concatenate([m[k] for m in mine]) for k in range(3))))
+    n_rows = sum(g[2].size for g in groups)
+    return {"seconds": dt, "threads": threads, "rows": n_rows,
+            "bytes": n_rows * q_row_bytes(4) * 2, "groups": per_group}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each token row "
+              "converts independently; sharding by heads or sequences needs no exchange). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import kv_cache_quantization_kvq_amd as kvq
+    from kv_cache_quantization_kvq_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(3)
+    kvq.load_library()                                   # fail loudly without the HIP library
+    dev_name = torch.cuda.get_device_name(0)
+    wl = PagedQ4(torch, kvq, synth)
+
+    # warmup (eager), also the parity reference for graph replays
+    for i in range(args.warmup):
+        wl.step(i % DRAWS)
+    torch.cuda.synchronize()
+
+    # graphs: steps spread round-robin over `--streams` independent chains
+    # (different steps touch different rows, so they need no ordering between
+    # them; within a step, dequantize follows its quantize on the same chain)
+    graphs = None
+    if not args.no_graph:
+        chains = [torch.cuda.Stream() for _ in range(args.streams)]
+        for c in chains:
+            c.wait_stream(torch.cuda.current_stream())
+        for d in range(DRAWS):
+            with torch.cuda.stream(chains[d % args.streams]):
+                wl.step(d)
+        for c in chains:
+            torch.cuda.current_stream().wait_stream(c)
+        torch.cuda.synchronize()
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cap = torch.cuda.current_stream()
+                for c in chains:
+                    c.wait_stream(cap)                       # fork
+                for d in range(n):
+                    with torch.cuda.stream(chains[d % args.streams]):
+                        wl.step(d)
+                for c in chains:
+                    cap.wait_stream(c)                       # join
+            return g
+
+        rem = args.steps % DRAWS
+        graphs = (capture(DRAWS), capture(rem) if rem else None)
+        graphs[0].replay()
+        torch.cuda.synchronize()
+
+    log("timing %d steps (%s) on %s" % (args.steps, "graph replay, %d chain(s)" % args.streams
+                                        if graphs else "eager", dev_name))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graphs:
+        for _ in range(args.steps // DRAWS):
+            graphs[0].replay()
+        if graphs[1] is not None:
+            graphs[1].replay()
+    else:
+        for i in range(args.steps):
+            wl.step(i % DRAWS)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    value = wl.bytes_per_step * args.steps / elapsed / 1e9
+
+    # per-kernel device durations (graph replays of each kernel alone)
+    reps = 4 * DRAWS
+    kt = time_kernels(torch, [("quant", wl.quant, list(range(DRAWS))),
+                              ("dequant", wl.dequant, list(range(DRAWS)))], reps)
+    dom = max(kt, key=kt.get)
+    achieved = wl.bytes_per_launch / kt[dom] / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom, wl.bytes_per_launch),
+                "kernel": ("quant_kv_kernel<4>" if dom == "quant" else "dequant_kv_kernel<4>"),
+                "bytes_per_launch": wl.bytes_per_launch,
+                "avg_us": {k: round(v * 1e6, 3) for k, v in kt.items()}}
+
+    # parity of the timed data: outputs of every draw against the oracle on a sample
+    import oracle
+
+    def rows_fn(t, rows):
+        idx = torch.from_numpy(np.asarray(rows, np.int64)).cuda()
+        x = t.view(t.shape[0] * t.shape[1], -1).index_select(0, idx)
+        a = x.cpu().numpy()
+        return a.view(np.uint16) if a.dtype == np.float16 else a
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on %d draws" % args.cpu_draws)
+        cb = cpu_baseline(wl, oracle, rows_fn, args.cpu_draws)
+        # the oracle's outputs against the device outputs of the same rows
+        for d, name, rows, c, sc, y in cb["groups"]:
+            q, s_, o = (wl.kq, wl.ks, wl.ko) if name == "K" else (wl.vq, wl.vs, wl.vo)
+            if not (np.array_equal(rows_fn(q, rows), c) and np.array_equal(rows_fn(s_, rows), sc)
+                    and np.array_equal(rows_fn(o, rows), y)):
+                log("PARITY FAILURE on the timed data (draw %d, %s)" % (d, name))
+                sys.exit(4)
+        log("timed data matches the oracle on %d rows" % cb["rows"])
+        cpu = {"value": round(cb["bytes"] / cb["seconds"] / 1e9, 4), "unit": "GB/s", "cores": cb["threads"],
+               "kind": "oracle",
+               "sample": "%d rows (K and V of %d paged-Q4 steps) quantized then dequantized by the "
+                         "scalar C oracle, rows split over %d threads, %.2f s wall"
+                         % (cb["rows"], args.cpu_draws, cb["threads"], cb["seconds"])}
+
+    secondary = None if args.no_secondary else secondary_workloads(torch, kvq, synth)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+
+    rec = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic", "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+           "elements_per_s": round(wl.elems_per_step * args.steps / elapsed, 1),
+           "config": {"workload": "paged_q4", "pages": wl.w.shape[0], "page_size": PAGE,
+                      "heads": HEADS, "head_dim": HEAD_DIM, "batch": wl.w.batch_size,
+                      "width": wl.w.width, "wbits": 4, "draws_rotated": DRAWS,
+                      "bytes_per_step": wl.bytes_per_step,
+                      "timed": ("graph, %d chains" % args.streams) if graphs else "eager",
+                      "device": dev_name},
+           "roofline": roofline, "cpu_baseline": cpu}
+    if secondary is not None:
+        rec["secondary"] = secondary
+    print(json.dumps(rec), flush=True)
+
+
+def traffic_for(kernel, algo_bytes):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_paged_q4.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("sources_sha256") != sources_digest():
+        return None
+    key = "%s_traffic_bytes_per_launch" % kernel
+    return float(kv[key]) if key in kv else None
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for f in ("kvq_kernels.hip", "kvq_device.h"):
+        with open(os.path.join(ROOT, "kv_cache_quantization_kvq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def secondary_workloads(torch, kvq, synth):
+    """Kernel-time GB/s of the other workloads (events around each launch)."""
+    t = torch
+    out = {}
+    # fp8 contiguous [1,256,8,128]
+    w = synth.fp8_contig()
+    x = t.from_numpy(w.k).cuda()
+    o8 = t.empty(w.shape, dtype=t.uint8, device="cuda")
+    ob = t.empty(w.shape, dtype=t.float16, device="cuda")
+    kt = time_kernels(t, [("to_fp8", lambda _: kvq.kvq_fp16_to_fp8(x, o8, 1, 0, 256), [0]),
+                          ("to_fp16", lambda _: kvq.kvq_fp8_to_fp16(o8, ob, 1, 0, 256), [0])], 64)
+    nb = 256 * ROW * 3
+    out["fp8_contig"] = {k: {"us": round(v * 1e6, 2), "GB/s": round(nb / v / 1e9, 1)} for k, v in kt.items()}
+    # Q4 contiguous window, Q6 contiguous
+    for name, fn, wb in (("q4_contig", synth.q4_contig, 4), ("q6_contig", synth.q6_contig, 6)):
+        w = fn()
+        k, v = t.from_numpy(w.k).cuda(), t.from_numpy(w.v).cuda()
+        cs, ss = kvq.code_shape(w.shape, wb), kvq.scale_shape(w.shape)
+        kq, vq = t.empty(cs, dtype=t.uint8, device="cuda"), t.empty(cs, dtype=t.uint8, device="cuda")
+        ks, vs = t.empty(ss, dtype=t.float16, device="cuda"), t.empty(ss, dtype=t.float16, device="cuda")
+        ko, vo = t.empty_like(k), t.empty_like(v)
+        a = (w.batch_size, w.offset, w.width)
+        kt = time_kernels(t, [
+            ("quant", lambda _: kvq.kvq_fp16_to_q_kv(k, kq, ks, v, vq, vs, *a, wbits=wb), [0]),
+            ("dequant", lambda _: kvq.kvq_q_to_fp16_kv(kq, ko, ks, vq, vo, vs, *a, wbits=wb), [0])], 32)
+        nb = 2 * w.batch_size * w.width * q_row_bytes(wb)
+        out[name] = {kk: {"us": round(vv * 1e6, 2), "GB/s": round(nb / vv / 1e9, 1)} for kk, vv in kt.items()}
+        del k, v, kq, vq, ks, vs, ko, vo
+    # paged K-Q4 + V-Q6 at 16384 pages (8 GiB per fp16 cache)
+    w = synth.mix_paged()
+    shape = w.shape
+    k = synth.device_normal_f16(t, shape, w.extra["device_seed"])
+    v = synth.device_normal_f16(t, shape, w.extra["device_seed"] + 1)
+    kq = t.empty(kvq.code_shape(shape, 4), dtype=t.uint8, device="cuda")
+    vq = t.empty(kvq.code_shape(shape, 6), dtype=t.uint8, device="cuda")
+    ks = t.empty(kvq.scale_shape(shape), dtype=t.float16, device="cuda")
+    vs = t.empty(kvq.scale_shape(shape), dtype=t.float16, device="cuda")
+    ko, vo = t.empty_like(k), t.empty_like(v)
+    sl, bt = t.from_numpy(w.cache_seqlens).cuda(), t.from_numpy(w.block_table).cuda()
+    a = (w.batch_size, w.offset, w.width, w.page_size, sl, bt)
+    kt = time_kernels(t, [
+        ("quant_k4", lambda _: kvq.kvq_fp16_to_q_kv(k, kq, ks, None, None, None, *a, 4), [0]),
+        ("quant_v6", lambda _: kvq.kvq_fp16_to_q_kv(None, None, None, v, vq, vs, *a, 6), [0]),
+        ("dequant_k4", lambda _: kvq.kvq_q_to_fp16_kv(kq, ko, ks, None, None, None, *a, 4), [0]),
+        ("dequant_v6", lambda _: kvq.kvq_q_to_fp16_kv(None, None, None, vq, vo, vs, *a, 6), [0])], 32)
+    rows = w.batch_size * w.width
+    nbs = {"quant_k4": rows * q_row_bytes(4), "dequant_k4": rows * q_row_bytes(4),
+           "quant_v6": rows * q_row_bytes(6), "dequant_v6": rows * q_row_bytes(6)}
+    out["mix_paged"] = {kk: {"us": round(vv * 1e6, 2), "GB/s": round(nbs[kk] / vv / 1e9, 1)} for kk, vv in kt.items()}
+    # a plain device copy moving the same bytes as one paged-Q4 launch
+    # (read half, write half): the practical bandwidth at this launch size
+    n = 2 * 32 * 256 * q_row_bytes(4) // 2 // 2
+    src = t.empty((DRAWS, n), dtype=t.float16, device="cuda")
+    dst = t.empty((DRAWS, n), dtype=t.float16, device="cuda")
+    kt = time_kernels(t, [("copy", lambda d: dst[d].copy_(src[d]), list(range(DRAWS)))], 4 * DRAWS)
+    out["copy_same_bytes"] = {"us": round(kt["copy"] * 1e6, 2), "GB/s": round(4 * n / kt["copy"] / 1e9, 1)}
+    del src, dst
+    ids_a, ids_b = w.extra["ids_a"], w.extra["ids_b"]
+    reps = 200
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        m = kvq.kvq_count_match(ids_a, ids_b, ids_a.size)
+    dt = (time.perf_counter() - t0) / reps
+    out["count_match"] = {"us": round(dt * 1e6, 2), "match": m, "n": int(ids_a.size)}
+    del k, v, kq, vq, ks, vs, ko, vo
+    torch.cuda.empty_cache()
+    return out
+
+
+def calibrate_copy(torch):
+    """A plain device-to-device copy of 1 GiB (fp16 elementwise copy kernel)
+    for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = (1 << 30) // 2
+    a = torch.ones(n, dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 x 1 GiB fp16 copies")
+
+
+if __name__ == "__main__":
+    main()

@@ -108,8 +108,9 @@ int q_call(bool quant, const void* k_src, void* k_dst, const void* k_scales, con
         if (!aligned(cache_seqlens, 4) || !aligned(block_table, 4)) return KVQ_ERR_ALIGN;
     }
     const int64_t R = (int64_t)s.heads * s.head_dim;
-    const int64_t nseg = (R / 8 + 127) / 128;
-    if ((int64_t)batch_size * width * nseg > INT32_MAX) return KVQ_ERR_RANGE;
+    // work units (row segments of K and V) are numbered in 32 bits
+    const int64_t max_seg = (R / 8 + 63) / 64;
+    if ((int64_t)batch_size * width * 2 * max_seg > INT32_MAX / 2) return KVQ_ERR_RANGE;
     const void* ptrs[6] = {k_src, k_dst, k_scales, v_src, v_dst, v_scales};
     for (const void* p : ptrs)
         if (p && !aligned(p, 16)) return KVQ_ERR_ALIGN;

@@ -19,10 +19,12 @@
 
 namespace kvq {
 
-constexpr int kWaves = 4;                 // wavefronts per workgroup
+#ifndef KVQ_WAVES_PER_BLOCK
+#define KVQ_WAVES_PER_BLOCK 4
+#endif
+constexpr int kWaves = KVQ_WAVES_PER_BLOCK;   // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kNch = 2;                   // chunks per lane per row segment
-constexpr int kSegChunks = 64 * kNch;     // 1024 elements per wave
+constexpr int kUnitsPerWave = 1;          // row segments converted per wavefront
 constexpr int kFp8Cpt = 4;                // chunks per thread, 8-bit kernels
 
 // ---------------------------------------------------------------- row map
@@ -52,6 +54,53 @@ __device__ __forceinline__ void prep_scale(uint32_t s16, float& s, float& r) {
     const bool zero = (sf == 0.0f);
     s = zero ? 1.0f : sf;
     r = zero ? 0.0f : __builtin_amdgcn_rcpf(sf);
+}
+
+// ---------------------------------------------------------------- work units
+//
+// A unit is one row segment of one tensor: (logical row n, tensor K or V,
+// segment g of NCH * 64 chunks).  Units are numbered with the segment
+// fastest, then the tensor, then the row, so consecutive units of a wave
+// share the row's paging lookup and touch neighbouring memory.  A wave takes
+// UPW consecutive units and issues all of their loads before converting the
+// first, so later loads are in flight while earlier units are computed.
+
+struct QGeom {
+    int32_t n_units;   // batch * width * ntens * nseg
+    int32_t nseg;      // row segments per row
+    int32_t ntens;     // tensors present: 1 or 2
+    int32_t tens0;     // the tensor when ntens == 1: 0 = K, 1 = V
+};
+
+struct UnitRef {
+    int64_t row;       // physical row (0 for a padding or skipped unit)
+    int32_t tensor;    // 0 = K, 1 = V
+    int32_t seg;
+    bool live;         // false: nothing to store
+};
+
+__device__ __forceinline__ UnitRef unit_ref(const QLaunch& a, const QGeom& g, int32_t u) {
+    UnitRef r;
+    r.live = u < g.n_units;
+    if (!r.live) u = g.n_units - 1;          // stay in bounds; the unit stores nothing
+    int32_t rt = u;
+    r.seg = 0;
+    if (g.nseg > 1) {
+        rt = u / g.nseg;
+        r.seg = u - rt * g.nseg;
+    }
+    int32_t n;
+    if (g.ntens == 2) {
+        n = rt >> 1;
+        r.tensor = rt & 1;
+    } else {
+        n = rt;
+        r.tensor = g.tens0;
+    }
+    const int64_t row = resolve_row(a, n);
+    r.live = r.live && row >= 0;
+    r.row = row >= 0 ? row : 0;               // a skipped row still loads row 0, in bounds
+    return r;
 }
 
 // ---------------------------------------------------------------- quantize
@@ -89,60 +138,47 @@ __device__ __forceinline__ void quant_store_chunk(uint4 x, int32_t c, bool activ
     if (active && (lane & 3) == 0) scales_row[c >> 2] = (uint16_t)s16;
 }
 
-template <int WBITS>
-__global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, int32_t nseg,
-                                                            int32_t n_units) {
+// UPW units per wave, NCH chunks per lane per unit; GUARD bounds-checks the
+// chunks of a partial last segment (rows whose chunk count is not a multiple
+// of NCH * 64).
+template <int WBITS, int UPW, int NCH, bool GUARD>
+__global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, QGeom g) {
     const int lane = threadIdx.x & 63;
-    const int32_t unit = (int32_t)blockIdx.x * kWaves +
+    const int32_t wave = (int32_t)blockIdx.x * kWaves +
                          __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    if (unit >= n_units) return;
-    int32_t n = unit, g = 0;
-    if (nseg > 1) {
-        n = unit / nseg;
-        g = unit - n * nseg;
-    }
-    const int64_t row = resolve_row(a, n);
-    if (row < 0) return;
-
+    const int32_t u0 = wave * UPW;
+    if (u0 >= g.n_units) return;
     const int32_t R = a.R;
     const int32_t cpr = R >> 3;
-    const int32_t cbase = g * kSegChunks + lane;
-    const int64_t elem0 = row * R;
-    const int64_t code0 = row * (int64_t)(R / 8 * WBITS);
-    const int64_t scale0 = row * (int64_t)(R >> 5);
 
-    const uint4* ksrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_src) + elem0);
-    const uint4* vsrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_src) + elem0);
-    const bool has_k = a.k_src != nullptr;
-    const bool has_v = a.v_src != nullptr;
-
-    uint4 kx[kNch], vx[kNch];
+    UnitRef ur[UPW];
 #pragma unroll
-    for (int k = 0; k < kNch; ++k) {
-        const int32_t c = cbase + k * 64;
-        kx[k] = make_uint4(0, 0, 0, 0);
-        vx[k] = make_uint4(0, 0, 0, 0);
-        if (c < cpr) {
-            if (has_k) kx[k] = ksrc[c];
-            if (has_v) vx[k] = vsrc[c];
+    for (int i = 0; i < UPW; ++i) ur[i] = unit_ref(a, g, u0 + i);
+
+    uint4 x[UPW][NCH];
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+        const uint16_t* base = static_cast<const uint16_t*>(ur[i].tensor ? a.v_src : a.k_src);
+        const uint4* src = reinterpret_cast<const uint4*>(base + ur[i].row * R);
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int32_t c = ur[i].seg * (NCH * 64) + k * 64 + lane;
+            if (GUARD) x[i][k] = c < cpr ? src[c] : make_uint4(0, 0, 0, 0);
+            else x[i][k] = src[c];
         }
     }
-    if (has_k) {
-        uint8_t* codes = static_cast<uint8_t*>(a.k_dst) + code0;
-        uint16_t* scales = static_cast<uint16_t*>(a.k_scales) + scale0;
+    // dead units (padding, skipped rows) are converted like the others and
+    // only their stores are masked off: no branch splits the load stream
 #pragma unroll
-        for (int k = 0; k < kNch; ++k) {
-            const int32_t c = cbase + k * 64;
-            quant_store_chunk<WBITS>(kx[k], c, c < cpr, lane, codes, scales);
-        }
-    }
-    if (has_v) {
-        uint8_t* codes = static_cast<uint8_t*>(a.v_dst) + code0;
-        uint16_t* scales = static_cast<uint16_t*>(a.v_scales) + scale0;
+    for (int i = 0; i < UPW; ++i) {
+        uint8_t* codes = static_cast<uint8_t*>(ur[i].tensor ? a.v_dst : a.k_dst) +
+                         ur[i].row * (int64_t)(R / 8 * WBITS);
+        uint16_t* scales = static_cast<uint16_t*>(ur[i].tensor ? a.v_scales : a.k_scales) +
+                           ur[i].row * (int64_t)(R >> 5);
 #pragma unroll
-        for (int k = 0; k < kNch; ++k) {
-            const int32_t c = cbase + k * 64;
-            quant_store_chunk<WBITS>(vx[k], c, c < cpr, lane, codes, scales);
+        for (int k = 0; k < NCH; ++k) {
+            const int32_t c = ur[i].seg * (NCH * 64) + k * 64 + lane;
+            quant_store_chunk<WBITS>(x[i][k], c, ur[i].live && (!GUARD || c < cpr), lane, codes, scales);
         }
     }
 }
@@ -151,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, int32_t n
 
 struct CodeChunk {
     uint32_t lo, hi;    // Q4: lo = 8 codes; Q6: 48-bit field (lo, hi16)
-    uint32_t s2;        // scale replicated in both halves
+    uint32_t s;         // scale (fp16 bits)
 };
 
 template <int WBITS>
@@ -163,78 +199,73 @@ __device__ __forceinline__ CodeChunk load_code_chunk(const uint8_t* __restrict__
         q.lo = reinterpret_cast<const uint32_t*>(codes_row)[c];
         q.hi = 0;
     } else {
-        // chunk c's 6 bytes start at 6c; load the 8 bytes of its 12-byte
-        // group that contain them (4-byte aligned) and shift odd chunks.
+        // chunk c's 6 bytes start at 6c: load the 8 bytes of its 12-byte
+        // group that contain them (4-byte aligned); odd chunks are shifted
+        // into place after the load.
         uint2 d;
         __builtin_memcpy(&d, codes_row + 12 * (c >> 1) + 4 * (c & 1), 8);
-        if (c & 1) {
-            q.lo = __builtin_amdgcn_alignbit(d.y, d.x, 16);
-            q.hi = d.y >> 16;
-        } else {
-            q.lo = d.x;
-            q.hi = d.y & 0xFFFFu;
-        }
+        q.lo = d.x;
+        q.hi = d.y;
     }
-    const uint32_t s = scales_row[c >> 2];
-    q.s2 = s | (s << 16);
+    q.s = scales_row[c >> 2];
     return q;
 }
 
 template <int WBITS>
-__device__ __forceinline__ uint4 dequant_chunk(const CodeChunk& q) {
-    if constexpr (WBITS == 4) return dequant_q4_chunk(q.lo, q.s2);
-    else return dequant_q6_chunk(q.lo, q.hi, q.s2);
+__device__ __forceinline__ uint4 dequant_chunk(const CodeChunk& q, int32_t c) {
+    const uint32_t s2 = q.s | (q.s << 16);
+    if constexpr (WBITS == 4) {
+        return dequant_q4_chunk(q.lo, s2);
+    } else {
+        uint32_t lo, hi;
+        if (c & 1) {
+            lo = __builtin_amdgcn_alignbit(q.hi, q.lo, 16);
+            hi = q.hi >> 16;
+        } else {
+            lo = q.lo;
+            hi = q.hi & 0xFFFFu;
+        }
+        return dequant_q6_chunk(lo, hi, s2);
+    }
 }
 
-template <int WBITS>
-__global__ __launch_bounds__(kThreads) void dequant_kv_kernel(QLaunch a, int32_t nseg,
-                                                              int32_t n_units) {
+template <int WBITS, int UPW, int NCH, bool GUARD>
+__global__ __launch_bounds__(kThreads) void dequant_kv_kernel(QLaunch a, QGeom g) {
     const int lane = threadIdx.x & 63;
-    const int32_t unit = (int32_t)blockIdx.x * kWaves +
+    const int32_t wave = (int32_t)blockIdx.x * kWaves +
                          __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    if (unit >= n_units) return;
-    int32_t n = unit, g = 0;
-    if (nseg > 1) {
-        n = unit / nseg;
-        g = unit - n * nseg;
-    }
-    const int64_t row = resolve_row(a, n);
-    if (row < 0) return;
-
+    const int32_t u0 = wave * UPW;
+    if (u0 >= g.n_units) return;
     const int32_t R = a.R;
     const int32_t cpr = R >> 3;
-    const int32_t cbase = g * kSegChunks + lane;
-    const int64_t elem0 = row * R;
-    const int64_t code0 = row * (int64_t)(R / 8 * WBITS);
-    const int64_t scale0 = row * (int64_t)(R >> 5);
-    const bool has_k = a.k_src != nullptr;
-    const bool has_v = a.v_src != nullptr;
 
-    CodeChunk kq[kNch], vq[kNch];
+    UnitRef ur[UPW];
 #pragma unroll
-    for (int k = 0; k < kNch; ++k) {
-        const int32_t c = cbase + k * 64;
-        kq[k] = CodeChunk{0, 0, 0};
-        vq[k] = CodeChunk{0, 0, 0};
-        if (c < cpr) {
-            if (has_k)
-                kq[k] = load_code_chunk<WBITS>(static_cast<const uint8_t*>(a.k_src) + code0,
-                                               static_cast<const uint16_t*>(a.k_scales) + scale0, c);
-            if (has_v)
-                vq[k] = load_code_chunk<WBITS>(static_cast<const uint8_t*>(a.v_src) + code0,
-                                               static_cast<const uint16_t*>(a.v_scales) + scale0, c);
+    for (int i = 0; i < UPW; ++i) ur[i] = unit_ref(a, g, u0 + i);
+
+    CodeChunk q[UPW][NCH];
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+        const uint8_t* codes = static_cast<const uint8_t*>(ur[i].tensor ? a.v_src : a.k_src) +
+                               ur[i].row * (int64_t)(R / 8 * WBITS);
+        const uint16_t* scales = static_cast<const uint16_t*>(ur[i].tensor ? a.v_scales : a.k_scales) +
+                                 ur[i].row * (int64_t)(R >> 5);
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int32_t c = ur[i].seg * (NCH * 64) + k * 64 + lane;
+            if (GUARD) q[i][k] = c < cpr ? load_code_chunk<WBITS>(codes, scales, c) : CodeChunk{0, 0, 0};
+            else q[i][k] = load_code_chunk<WBITS>(codes, scales, c);
         }
     }
 #pragma unroll
-    for (int k = 0; k < kNch; ++k) {
-        const int32_t c = cbase + k * 64;
-        if (c < cpr) {
-            if (has_k)
-                reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_dst) + elem0)[c] =
-                    dequant_chunk<WBITS>(kq[k]);
-            if (has_v)
-                reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_dst) + elem0)[c] =
-                    dequant_chunk<WBITS>(vq[k]);
+    for (int i = 0; i < UPW; ++i) {
+        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(ur[i].tensor ? a.v_dst : a.k_dst) +
+                                              ur[i].row * R);
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int32_t c = ur[i].seg * (NCH * 64) + k * 64 + lane;
+            const uint4 o = dequant_chunk<WBITS>(q[i][k], c);
+            if (ur[i].live && (!GUARD || c < cpr)) dst[c] = o;
         }
     }
 }
@@ -351,34 +382,52 @@ int launch_fp8_to_fp16(const Fp8Launch& a, void* stream) {
     return launch(reinterpret_cast<const void*>(&fp8_to_fp16_kernel), fp8_grid(a), dim3(kThreads), args, stream);
 }
 
-static void q_geometry(const QLaunch& a, int32_t& nseg, int32_t& n_units, dim3& grid) {
+// Kernel variant for a call: the unguarded fast path needs every segment
+// full (row chunk count a multiple of NCH * 64).
+template <int WBITS, bool QUANT>
+static const void* q_kernel(int nch, bool guard) {
+    constexpr int U = kUnitsPerWave;
+    if (QUANT) {
+        if (guard) return reinterpret_cast<const void*>(&quant_kv_kernel<WBITS, 1, 2, true>);
+        if (nch == 2) return reinterpret_cast<const void*>(&quant_kv_kernel<WBITS, U, 2, false>);
+        return reinterpret_cast<const void*>(&quant_kv_kernel<WBITS, U, 1, false>);
+    }
+    if (guard) return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, 1, 2, true>);
+    if (nch == 2) return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, U, 2, false>);
+    return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, U, 1, false>);
+}
+
+static int launch_q(const QLaunch& a, bool quant, void* stream) {
     const int32_t cpr = a.R >> 3;
-    nseg = (cpr + kSegChunks - 1) / kSegChunks;
-    n_units = (int32_t)((int64_t)a.batch * a.width * nseg);   // bounded by the host checks
-    grid = dim3((unsigned)((n_units + kWaves - 1) / kWaves), 1, 1);
-}
-
-int launch_quant_kv(const QLaunch& a, void* stream) {
+    int nch = 2;
+    bool guard = false;
+    int upw = kUnitsPerWave;
+    if (cpr % 128 == 0) {
+        nch = 2;
+    } else if (cpr % 64 == 0) {
+        nch = 1;
+    } else {
+        guard = true;
+        upw = 1;
+    }
+    QGeom g;
+    g.nseg = (cpr + nch * 64 - 1) / (nch * 64);
+    g.ntens = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
+    g.tens0 = a.k_src ? 0 : 1;
+    g.n_units = (int32_t)((int64_t)a.batch * a.width * g.ntens * g.nseg);   // bounded by the host checks
+    const int64_t waves = (g.n_units + upw - 1) / upw;
+    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     QLaunch arg = a;
-    int32_t nseg, n_units;
-    dim3 grid;
-    q_geometry(a, nseg, n_units, grid);
-    void* args[] = {&arg, &nseg, &n_units};
-    const void* fn = a.wbits == 4 ? reinterpret_cast<const void*>(&quant_kv_kernel<4>)
-                                  : reinterpret_cast<const void*>(&quant_kv_kernel<6>);
+    void* args[] = {&arg, &g};
+    const void* fn;
+    if (a.wbits == 4) fn = quant ? q_kernel<4, true>(nch, guard) : q_kernel<4, false>(nch, guard);
+    else fn = quant ? q_kernel<6, true>(nch, guard) : q_kernel<6, false>(nch, guard);
     return launch(fn, grid, dim3(kThreads), args, stream);
 }
 
-int launch_dequant_kv(const QLaunch& a, void* stream) {
-    QLaunch arg = a;
-    int32_t nseg, n_units;
-    dim3 grid;
-    q_geometry(a, nseg, n_units, grid);
-    void* args[] = {&arg, &nseg, &n_units};
-    const void* fn = a.wbits == 4 ? reinterpret_cast<const void*>(&dequant_kv_kernel<4>)
-                                  : reinterpret_cast<const void*>(&dequant_kv_kernel<6>);
-    return launch(fn, grid, dim3(kThreads), args, stream);
-}
+int launch_quant_kv(const QLaunch& a, void* stream) { return launch_q(a, true, stream); }
+
+int launch_dequant_kv(const QLaunch& a, void* stream) { return launch_q(a, false, stream); }
 
 int launch_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s, int64_t ns, int wbits,
                           bool force_clamp, uint8_t* u, void* stream) {

@@ -377,3 +377,48 @@ def test_fp8_ragged(kvq, heads, head_dim):
     x = rng.standard_normal(shape).astype(np.float16)
     for batch, offset, width in ((4, 0, 9), (3, 2, 5), (1, 8, 1)):
         _fp8_roundtrip(kvq, x, batch, offset, width, "fp8 %s" % (shape,))
+
+
+# ---------------------------------------------------------------- graph replay
+def test_graph_replay_matches_eager(kvq):
+    """The paged Q4 step captured in a HIP graph: every replay (with eager
+    work and synchronisation between replays) reproduces the eager bytes."""
+    t = torch()
+    rng = np.random.default_rng(99)
+    num_pages, ps = 64, 16
+    shape = (num_pages, ps, 8, 128)
+    k = dev(rng.standard_normal(shape).astype(np.float16))
+    v = dev(rng.standard_normal(shape).astype(np.float16))
+    bt = dev(rng.permutation(num_pages).astype(np.int32)[:32].reshape(4, 8))
+    sl = dev(np.array([0, 17, 60, 100], np.int32))
+    outs = [t.zeros(_cs(shape, 4), dtype=t.uint8, device="cuda"),
+            t.zeros(_ss(shape), dtype=t.float16, device="cuda"),
+            t.zeros(_cs(shape, 4), dtype=t.uint8, device="cuda"),
+            t.zeros(_ss(shape), dtype=t.float16, device="cuda"),
+            t.zeros(shape, dtype=t.float16, device="cuda"),
+            t.zeros(shape, dtype=t.float16, device="cuda")]
+    kq, ks, vq, vs, ko, vo = outs
+
+    def step():
+        kvq.kvq_fp16_to_q_kv(k, kq, ks, v, vq, vs, 4, 0, 20, ps, sl, bt, 4)
+        kvq.kvq_q_to_fp16_kv(kq, ko, ks, vq, vo, vs, 4, 0, 20, ps, sl, bt, 4)
+
+    step()
+    ref = [host(o).copy() for o in outs]
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(s):
+        step()
+    t.cuda.current_stream().wait_stream(s)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            byte_diff(host(o), r, "graph replay %d" % rep)
