@@ -63,6 +63,27 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
     return v > o ? v : o;
 }
 
+// Max over a lane pair (lanes 2m, 2m+1), both active together.
+__device__ __forceinline__ uint32_t pair_max(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false);
+    return v > o ? v : o;
+}
+
+// Largest |x| of the 16 fp16 values of two chunks, as fp16 bits.
+__device__ __forceinline__ uint32_t absmax_2chunks(uint4 v, uint4 w) {
+    u16x2_t m0 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu),
+                                           __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu));
+    u16x2_t m1 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu),
+                                           __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu));
+    u16x2_t m2 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, w.x & 0x7FFF7FFFu),
+                                           __builtin_bit_cast(u16x2_t, w.y & 0x7FFF7FFFu));
+    u16x2_t m3 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, w.z & 0x7FFF7FFFu),
+                                           __builtin_bit_cast(u16x2_t, w.w & 0x7FFF7FFFu));
+    u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
+                                          __builtin_elementwise_max(m2, m3));
+    return (uint32_t)(m.x > m.y ? m.x : m.y);
+}
+
 // Value of the partner lane (lane ^ 1).
 __device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false);
@@ -98,57 +119,119 @@ __device__ __forceinline__ float mul_f16hi(uint32_t w, float r) {
     return y;
 }
 
+// Operands derived once per block from its stored scale s16.
+struct ScaleOps {
+    float s;        // scale (1 for a zero scale)
+    float r;        // rcp(s), within 1 ulp of 1/s (0 for a zero scale)
+    uint32_t r2;    // fp16(r) in both halves; used only for normal scales
+};
+
+// A zero scale maps every element to q = 0: with (s, r) = (1, 0) the
+// quotient below is 0 for every finite x.
+__device__ __forceinline__ ScaleOps prep_scale(uint32_t s16) {
+    const float sf = h2f(s16);
+    const bool zero = (sf == 0.0f);
+    ScaleOps o;
+    o.s = zero ? 1.0f : sf;
+    o.r = zero ? 0.0f : __builtin_amdgcn_rcpf(sf);
+    const uint32_t r16 = f2h(o.r);
+    o.r2 = r16 | (r16 << 16);
+    return o;
+}
+
 // Code of one element; the low WBITS bits of the result are u = q + Z, the
 // bits from 24 up hold the exponent of the rounding constant (bits WBITS..23
 // are zero).
 //
-// q = round_half_even(x / s) is obtained without a divide:
-//   y  = x * r                r = rcp(s), within 1 ulp of 1/s
-//   e  = fma(-y, s, x)        exact residual x - y*s
-//   y2 = fma(e, r, y)         corrected quotient
+// q = round_half_even(x / s) is obtained without a divide, from a first
+// quotient y refined by one exact residual:
+//   e  = fma(-y, s, x)        exact: y*s is within a few ulp of x
+//   y2 = fma(e, r, y)         r = rcp(s), within 1 ulp of 1/s
 // For fp16 x and s, x/s is either an exact half-integer tie (then y2 lands
-// on it exactly, the correction being far below half an ulp) or lies at
-// least ~2^-13 relative from any tie, far beyond the few-ulp error of y2;
-// so rounding y2 gives round_half_even(x / s) on every pair.
+// on it exactly: the correction's own error is far below half an ulp) or
+// lies at least ~2^-13 relative from any tie, far beyond the few-ulp error
+// of y2; so rounding y2 gives round_half_even(x / s) on every pair.
 // Adding M = 2^23 + Z rounds to an integer with ties-to-even (the fp32 ulp
 // in [2^23, 2^24) is 1; Z is even, so parity is kept) and leaves u in the
 // low mantissa bits.
-// The clamp to [-Z, Z-1] (which commutes with rounding: integer bounds) can
-// only act when s is an fp16 subnormal: a normal s16 = fp16_rne(a / Q) is at
-// least (a / Q) * (1 - 2^-11), so every element of its block has
-// |x / s16| <= Q * (1 + 2^-10) < Q + 1/2, which keeps y2 + M inside
-// [2^23, 2^24) and the rounded code inside [-Q, Q].  Without the clamp the
-// routine is therefore only valid on that domain.
-template <int WBITS, bool CLAMP>
-__device__ __forceinline__ uint32_t quant_elem(float y, uint32_t w, bool hi, float s, float r) {
-    constexpr float Z = (float)(1 << (WBITS - 1));
-    constexpr float M = 8388608.0f + Z;
-    float e;
-    if (hi)
-        asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(e) : "v"(y), "v"(s), "v"(w));
-    else
-        asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel_hi:[0,0,1]" : "=v"(e) : "v"(y), "v"(s), "v"(w));
-    float y2 = __builtin_fmaf(e, r, y);
-    if (CLAMP) y2 = __builtin_amdgcn_fmed3f(y2, -Z, Z - 1.0f);
-    return __builtin_bit_cast(uint32_t, y2 + M);
+//
+// Two paths, chosen per block:
+//  - normal scale (s16 >= 2^-14): the first quotient is one packed fp16
+//    multiply y = fp16(x * fp16(r)) for two elements (relative error below
+//    2^-9; the residual x - y*s then still fits 24 bits, so e is exact), and
+//    no clamp: a normal s16 = fp16_rne(a / Q) is at least (a / Q)(1 - 2^-11),
+//    so every element of its block has |x / s16| <= Q (1 + 2^-10) < Q + 1/2,
+//    which keeps y2 + M in [2^23, 2^24) and the code in [-Q, Q];
+//  - subnormal or zero scale: y = x * r in fp32 and the clamp to [-Z, Z-1]
+//    (which commutes with rounding: integer bounds).
+// The normal path is only valid on that domain (|x / s| < Q + 1/2).
+
+// e = fma(-y, s, x) and y2 = fma(e, r, y) with y an fp16 half of yw and x an
+// fp16 half of xw (HI selects the high halves), in two v_fma_mix_f32.
+template <bool HI>
+__device__ __forceinline__ float refine_h(uint32_t yw, uint32_t xw, float s, float r) {
+    float e, y2;
+    if (HI) {
+        asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(e) : "v"(yw), "v"(s), "v"(xw));
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(y2) : "v"(e), "v"(r), "v"(yw));
+    } else {
+        asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel_hi:[1,0,1]" : "=v"(e) : "v"(yw), "v"(s), "v"(xw));
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,0,1]" : "=v"(y2) : "v"(e), "v"(r), "v"(yw));
+    }
+    return y2;
 }
 
-// 8 codes of a chunk, code j in the low WBITS bits of u[j].
-template <int WBITS, bool CLAMP>
-__device__ __forceinline__ void quant_chunk_impl(uint4 v, float s, float r, uint32_t (&u)[8]) {
+// Same refinement with an fp32 first quotient y (x an fp16 half of xw).
+template <bool HI>
+__device__ __forceinline__ float refine_f(float y, uint32_t xw, float s, float r) {
+    float e;
+    if (HI)
+        asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(e) : "v"(y), "v"(s), "v"(xw));
+    else
+        asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel_hi:[0,0,1]" : "=v"(e) : "v"(y), "v"(s), "v"(xw));
+    return __builtin_fmaf(e, r, y);
+}
+
+template <int WBITS>
+__device__ __forceinline__ uint32_t round_code(float y2) {
+    constexpr float Z = (float)(1 << (WBITS - 1));
+    return __builtin_bit_cast(uint32_t, y2 + (8388608.0f + Z));
+}
+
+template <int WBITS>
+__device__ __forceinline__ uint32_t round_code_clamped(float y2) {
+    constexpr float Z = (float)(1 << (WBITS - 1));
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(y2, -Z, Z - 1.0f) + (8388608.0f + Z));
+}
+
+// Normal-scale path for the 8 elements of a chunk.
+template <int WBITS>
+__device__ __forceinline__ void quant_chunk_normal(uint4 v, const ScaleOps& so, uint32_t (&u)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        u[2 * i] = quant_elem<WBITS, CLAMP>(mul_f16lo(w[i], r), w[i], false, s, r);
-        u[2 * i + 1] = quant_elem<WBITS, CLAMP>(mul_f16hi(w[i], r), w[i], true, s, r);
+        const uint32_t yw = as_u32(as_h2(w[i]) * as_h2(so.r2));
+        u[2 * i] = round_code<WBITS>(refine_h<false>(yw, w[i], so.s, so.r));
+        u[2 * i + 1] = round_code<WBITS>(refine_h<true>(yw, w[i], so.s, so.r));
     }
 }
 
-// s16 is the block's stored scale (fp16 bits); (s, r) from prep_scale.
+// Clamping path (subnormal or zero scale; defined on every finite pair).
 template <int WBITS>
-__device__ __forceinline__ void quant_chunk(uint4 v, uint32_t s16, float s, float r, uint32_t (&u)[8]) {
-    if (s16 >= 0x0400u) quant_chunk_impl<WBITS, false>(v, s, r, u);
-    else quant_chunk_impl<WBITS, true>(v, s, r, u);
+__device__ __forceinline__ void quant_chunk_clamped(uint4 v, const ScaleOps& so, uint32_t (&u)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        u[2 * i] = round_code_clamped<WBITS>(refine_f<false>(mul_f16lo(w[i], so.r), w[i], so.s, so.r));
+        u[2 * i + 1] = round_code_clamped<WBITS>(refine_f<true>(mul_f16hi(w[i], so.r), w[i], so.s, so.r));
+    }
+}
+
+// The kernels' dispatch: s16 is the block's stored scale (fp16 bits).
+template <int WBITS>
+__device__ __forceinline__ void quant_chunk(uint4 v, uint32_t s16, const ScaleOps& so, uint32_t (&u)[8]) {
+    if (s16 >= 0x0400u) quant_chunk_normal<WBITS>(v, so, u);
+    else quant_chunk_clamped<WBITS>(v, so, u);
 }
 
 // 4-bit: code j at bits 4j..4j+3 of one little-endian word.  Codes 2..7

@@ -24,8 +24,32 @@ namespace kvq {
 #endif
 constexpr int kWaves = KVQ_WAVES_PER_BLOCK;   // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kUnitsPerWave = 1;          // row segments converted per wavefront
 constexpr int kFp8Cpt = 4;                // chunks per thread, 8-bit kernels
+
+// ---------------------------------------------------------------- memory policy
+//
+// Data read once or written for later use elsewhere are accessed with the
+// non-temporal hint ("nt": streamed through the caches with low retention):
+// the source of every conversion (fp16 rows to quantize or narrow, codes,
+// scales and bytes to widen back) and the fp16 rows written by dequantize
+// and by 8-bit -> fp16.  The compact outputs (codes, scales, 8-bit bytes) use
+// ordinary stores, so an immediately following inverse conversion of the
+// same rows finds them in cache.  (Measured on MI355X at the paged Q4
+// workload: a quantize + dequantize step goes from 23.5 us with ordinary
+// accesses to 19.6 us.)
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint32_t ld_nt(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_nt(uint4* p, uint4 v) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
 
 // ---------------------------------------------------------------- row map
 
@@ -34,10 +58,11 @@ constexpr int kFp8Cpt = 4;                // chunks per thread, 8-bit kernels
 // offset + t in page block_table[b][p / page_size], slot p % page_size;
 // skipped if p < 0, past the table, or the page is outside [0, dim0).
 // All values are wave-uniform (scalar loads and SALU).
+template <bool PAGED>
 __device__ __forceinline__ int64_t resolve_row(const QLaunch& a, int32_t n) {
     const int32_t b = n / a.width;
     const int32_t t = n - b * a.width;
-    if (a.page_size == 0) return (int64_t)b * a.dim1 + a.offset + t;
+    if (!PAGED) return (int64_t)b * a.dim1 + a.offset + t;
     const int64_t p = (int64_t)a.cache_seqlens[b] + a.offset + t;
     if (p < 0 || p >= (int64_t)a.bt_cols * a.page_size) return -1;
     const uint32_t pu = (uint32_t)p;
@@ -47,23 +72,12 @@ __device__ __forceinline__ int64_t resolve_row(const QLaunch& a, int32_t n) {
     return (int64_t)page * a.page_size + (int64_t)(pu - pi * (uint32_t)a.page_size);
 }
 
-// Scale operands for the element routine.  A zero scale maps every element
-// to q = 0: with (s, r) = (1, 0), y = 0, e = x and y2 = 0.
-__device__ __forceinline__ void prep_scale(uint32_t s16, float& s, float& r) {
-    const float sf = h2f(s16);
-    const bool zero = (sf == 0.0f);
-    s = zero ? 1.0f : sf;
-    r = zero ? 0.0f : __builtin_amdgcn_rcpf(sf);
-}
-
 // ---------------------------------------------------------------- work units
 //
 // A unit is one row segment of one tensor: (logical row n, tensor K or V,
-// segment g of NCH * 64 chunks).  Units are numbered with the segment
-// fastest, then the tensor, then the row, so consecutive units of a wave
-// share the row's paging lookup and touch neighbouring memory.  A wave takes
-// UPW consecutive units and issues all of their loads before converting the
-// first, so later loads are in flight while earlier units are computed.
+// segment g).  Units are numbered with the segment fastest, then the tensor,
+// then the row, so neighbouring waves share the row's paging lookup and
+// touch neighbouring memory.  One wavefront converts one unit.
 
 struct QGeom {
     int32_t n_units;   // batch * width * ntens * nseg
@@ -79,10 +93,14 @@ struct UnitRef {
     bool live;         // false: nothing to store
 };
 
+// Dead units (grid padding past n_units, skipped rows) still read row 0 of
+// their tensor (always in bounds) and only have their stores masked off, so
+// no branch splits a wave's load stream.
+template <bool PAGED>
 __device__ __forceinline__ UnitRef unit_ref(const QLaunch& a, const QGeom& g, int32_t u) {
     UnitRef r;
     r.live = u < g.n_units;
-    if (!r.live) u = g.n_units - 1;          // stay in bounds; the unit stores nothing
+    if (!r.live) u = g.n_units - 1;
     int32_t rt = u;
     r.seg = 0;
     if (g.nseg > 1) {
@@ -97,96 +115,68 @@ __device__ __forceinline__ UnitRef unit_ref(const QLaunch& a, const QGeom& g, in
         n = rt;
         r.tensor = g.tens0;
     }
-    const int64_t row = resolve_row(a, n);
+    const int64_t row = resolve_row<PAGED>(a, n);
     r.live = r.live && row >= 0;
-    r.row = row >= 0 ? row : 0;               // a skipped row still loads row 0, in bounds
+    r.row = row >= 0 ? row : 0;
     return r;
 }
 
 // ---------------------------------------------------------------- quantize
-
-template <int WBITS>
-__device__ __forceinline__ void quant_store_chunk(uint4 x, int32_t c, bool active, int lane,
-                                                  uint8_t* __restrict__ codes_row,
-                                                  uint16_t* __restrict__ scales_row) {
-    const uint32_t s16 = scale_from_absmax<WBITS>(quad_max(absmax_chunk(x)));
-    float s, r;
-    prep_scale(s16, s, r);
-    uint32_t u[8];
-    quant_chunk<WBITS>(x, s16, s, r, u);
-    if constexpr (WBITS == 4) {
-        const uint32_t w = pack_q4(u);
-        if (active) reinterpret_cast<uint32_t*>(codes_row)[c] = w;
-    } else {
-        uint32_t lo, hi;
-        pack_q6(u, lo, hi);
-        // lanes 2m, 2m+1 own one 12-byte group: the even lane writes bytes
-        // 0..7, the odd lane bytes 8..11.
-        const uint32_t partner_lo = pair_swap(lo);
-        if (active) {
-            if ((lane & 1) == 0) {
-                uint2 d;
-                d.x = lo;
-                d.y = __builtin_amdgcn_perm(partner_lo, hi, 0x05040100u);   // hi.lo16 | partner.lo16 << 16
-                __builtin_memcpy(codes_row + 6 * c, &d, 8);   // 4-byte aligned
-            } else {
-                const uint32_t d = __builtin_amdgcn_alignbit(hi, lo, 16);   // lo >> 16 | hi << 16
-                *reinterpret_cast<uint32_t*>(codes_row + 6 * c + 2) = d;
-            }
-        }
-    }
-    if (active && (lane & 3) == 0) scales_row[c >> 2] = (uint16_t)s16;
-}
-
-// UPW units per wave, NCH chunks per lane per unit; GUARD bounds-checks the
-// chunks of a partial last segment (rows whose chunk count is not a multiple
-// of NCH * 64).
-template <int WBITS, int UPW, int NCH, bool GUARD>
+//
+// Lane l of segment g owns the 16 consecutive elements of piece
+// pc = 64 g + l (two 128-bit loads); a 32-element block is one lane pair, so
+// the block absmax is one DPP exchange.  A segment is 1024 elements; GUARD
+// masks the pieces past the row end of a partial last segment (pieces per
+// row are even, so a lane pair is in or out together).
+template <int WBITS, bool PAGED, bool GUARD>
 __global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, QGeom g) {
     const int lane = threadIdx.x & 63;
     const int32_t wave = (int32_t)blockIdx.x * kWaves +
                          __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int32_t u0 = wave * UPW;
-    if (u0 >= g.n_units) return;
+    const UnitRef ur = unit_ref<PAGED>(a, g, wave);
     const int32_t R = a.R;
-    const int32_t cpr = R >> 3;
+    const int32_t pc = ur.seg * 64 + lane;
+    const bool in = !GUARD || pc < (R >> 4);
 
-    UnitRef ur[UPW];
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) ur[i] = unit_ref(a, g, u0 + i);
+    const uint4* src = reinterpret_cast<const uint4*>(
+        static_cast<const uint16_t*>(ur.tensor ? a.v_src : a.k_src) + ur.row * R) + 2 * pc;
+    uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
+    if (in) {
+        x0 = ld_nt(src);
+        x1 = ld_nt(src + 1);
+    }
+    const uint32_t s16 = scale_from_absmax<WBITS>(pair_max(absmax_2chunks(x0, x1)));
+    const ScaleOps so = prep_scale(s16);
+    uint32_t u0[8], u1[8];
+    quant_chunk<WBITS>(x0, s16, so, u0);
+    quant_chunk<WBITS>(x1, s16, so, u1);
 
-    uint4 x[UPW][NCH];
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-        const uint16_t* base = static_cast<const uint16_t*>(ur[i].tensor ? a.v_src : a.k_src);
-        const uint4* src = reinterpret_cast<const uint4*>(base + ur[i].row * R);
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int32_t c = ur[i].seg * (NCH * 64) + k * 64 + lane;
-            if (GUARD) x[i][k] = c < cpr ? src[c] : make_uint4(0, 0, 0, 0);
-            else x[i][k] = src[c];
-        }
+    const bool store = ur.live && in;
+    uint8_t* codes = static_cast<uint8_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * (int64_t)(R / 8 * WBITS);
+    if constexpr (WBITS == 4) {
+        const uint2 d = make_uint2(pack_q4(u0), pack_q4(u1));
+        if (store) *reinterpret_cast<uint2*>(codes + 8 * pc) = d;
+    } else {
+        uint32_t lo0, hi0, lo1, hi1;
+        pack_q6(u0, lo0, hi0);
+        pack_q6(u1, lo1, hi1);
+        uint32_t d[3];
+        d[0] = lo0;
+        d[1] = __builtin_amdgcn_perm(lo1, hi0, 0x05040100u);   // hi0.lo16 | lo1.lo16 << 16
+        d[2] = __builtin_amdgcn_alignbit(hi1, lo1, 16);        // lo1 >> 16 | hi1 << 16
+        if (store) __builtin_memcpy(codes + 12 * pc, d, 12);    // 4-byte aligned
     }
-    // dead units (padding, skipped rows) are converted like the others and
-    // only their stores are masked off: no branch splits the load stream
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-        uint8_t* codes = static_cast<uint8_t*>(ur[i].tensor ? a.v_dst : a.k_dst) +
-                         ur[i].row * (int64_t)(R / 8 * WBITS);
-        uint16_t* scales = static_cast<uint16_t*>(ur[i].tensor ? a.v_scales : a.k_scales) +
-                           ur[i].row * (int64_t)(R >> 5);
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int32_t c = ur[i].seg * (NCH * 64) + k * 64 + lane;
-            quant_store_chunk<WBITS>(x[i][k], c, ur[i].live && (!GUARD || c < cpr), lane, codes, scales);
-        }
-    }
+    uint16_t* scales = static_cast<uint16_t*>(ur.tensor ? a.v_scales : a.k_scales) + ur.row * (int64_t)(R >> 5);
+    if (store && (lane & 1) == 0) scales[pc >> 1] = (uint16_t)s16;
 }
 
 // ---------------------------------------------------------------- dequantize
+//
+// Lane l holds chunks (8 elements) c = NCH * 64 g + 64 k + l, k < NCH, so
+// every 128-bit store of the wave is contiguous.
 
 struct CodeChunk {
-    uint32_t lo, hi;    // Q4: lo = 8 codes; Q6: 48-bit field (lo, hi16)
+    uint32_t lo, hi;    // Q4: lo = 8 codes; Q6: the 8 bytes holding the 6 code bytes
     uint32_t s;         // scale (fp16 bits)
 };
 
@@ -196,18 +186,17 @@ __device__ __forceinline__ CodeChunk load_code_chunk(const uint8_t* __restrict__
                                                      int32_t c) {
     CodeChunk q;
     if constexpr (WBITS == 4) {
-        q.lo = reinterpret_cast<const uint32_t*>(codes_row)[c];
+        q.lo = ld_nt(reinterpret_cast<const uint32_t*>(codes_row) + c);
         q.hi = 0;
     } else {
         // chunk c's 6 bytes start at 6c: load the 8 bytes of its 12-byte
         // group that contain them (4-byte aligned); odd chunks are shifted
         // into place after the load.
-        uint2 d;
-        __builtin_memcpy(&d, codes_row + 12 * (c >> 1) + 4 * (c & 1), 8);
-        q.lo = d.x;
-        q.hi = d.y;
+        const uint32_t* g = reinterpret_cast<const uint32_t*>(codes_row + 12 * (c >> 1) + 4 * (c & 1));
+        q.lo = ld_nt(g);
+        q.hi = ld_nt(g + 1);
     }
-    q.s = scales_row[c >> 2];
+    q.s = ld_nt(scales_row + (c >> 2));
     return q;
 }
 
@@ -229,43 +218,32 @@ __device__ __forceinline__ uint4 dequant_chunk(const CodeChunk& q, int32_t c) {
     }
 }
 
-template <int WBITS, int UPW, int NCH, bool GUARD>
+template <int WBITS, bool PAGED, int NCH, bool GUARD>
 __global__ __launch_bounds__(kThreads) void dequant_kv_kernel(QLaunch a, QGeom g) {
     const int lane = threadIdx.x & 63;
     const int32_t wave = (int32_t)blockIdx.x * kWaves +
                          __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int32_t u0 = wave * UPW;
-    if (u0 >= g.n_units) return;
+    const UnitRef ur = unit_ref<PAGED>(a, g, wave);
     const int32_t R = a.R;
     const int32_t cpr = R >> 3;
-
-    UnitRef ur[UPW];
+    const uint8_t* codes = static_cast<const uint8_t*>(ur.tensor ? a.v_src : a.k_src) +
+                           ur.row * (int64_t)(R / 8 * WBITS);
+    const uint16_t* scales = static_cast<const uint16_t*>(ur.tensor ? a.v_scales : a.k_scales) +
+                             ur.row * (int64_t)(R >> 5);
+    CodeChunk q[NCH];
 #pragma unroll
-    for (int i = 0; i < UPW; ++i) ur[i] = unit_ref(a, g, u0 + i);
-
-    CodeChunk q[UPW][NCH];
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-        const uint8_t* codes = static_cast<const uint8_t*>(ur[i].tensor ? a.v_src : a.k_src) +
-                               ur[i].row * (int64_t)(R / 8 * WBITS);
-        const uint16_t* scales = static_cast<const uint16_t*>(ur[i].tensor ? a.v_scales : a.k_scales) +
-                                 ur[i].row * (int64_t)(R >> 5);
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int32_t c = ur[i].seg * (NCH * 64) + k * 64 + lane;
-            if (GUARD) q[i][k] = c < cpr ? load_code_chunk<WBITS>(codes, scales, c) : CodeChunk{0, 0, 0};
-            else q[i][k] = load_code_chunk<WBITS>(codes, scales, c);
-        }
+    for (int k = 0; k < NCH; ++k) {
+        const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
+        if (GUARD) q[k] = c < cpr ? load_code_chunk<WBITS>(codes, scales, c) : CodeChunk{0, 0, 0};
+        else q[k] = load_code_chunk<WBITS>(codes, scales, c);
     }
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * R);
 #pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(ur[i].tensor ? a.v_dst : a.k_dst) +
-                                              ur[i].row * R);
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int32_t c = ur[i].seg * (NCH * 64) + k * 64 + lane;
-            const uint4 o = dequant_chunk<WBITS>(q[i][k], c);
-            if (ur[i].live && (!GUARD || c < cpr)) dst[c] = o;
+    for (int k = 0; k < NCH; ++k) {
+        const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
+        const uint4 o = dequant_chunk<WBITS>(q[k], c);
+        if (ur.live && (!GUARD || c < cpr)) {
+            st_nt(dst + c, o);
         }
     }
 }
@@ -292,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void fp16_to_fp8_kernel(Fp8Launch a) {
 #pragma unroll
         for (int k = 0; k < kFp8Cpt; ++k) {
             const int64_t c = c0 + k * kThreads;
-            v[k] = c < cps ? src[c] : make_uint4(0, 0, 0, 0);
+            v[k] = c < cps ? ld_nt(src + c) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int k = 0; k < kFp8Cpt; ++k) {
@@ -313,13 +291,15 @@ __global__ __launch_bounds__(kThreads) void fp8_to_fp16_kernel(Fp8Launch a) {
 #pragma unroll
         for (int k = 0; k < kFp8Cpt; ++k) {
             const int64_t c = c0 + k * kThreads;
-            v[k] = c < cps ? src[c] : make_uint2(0, 0);
+            v[k] = c < cps ? make_uint2(ld_nt(reinterpret_cast<const uint32_t*>(src + c)),
+                                        ld_nt(reinterpret_cast<const uint32_t*>(src + c) + 1))
+                           : make_uint2(0, 0);
         }
 #pragma unroll
         for (int k = 0; k < kFp8Cpt; ++k) {
             const int64_t c = c0 + k * kThreads;
             if (c < cps)
-                dst[c] = make_uint4(widen_lo(v[k].x), widen_hi(v[k].x), widen_lo(v[k].y), widen_hi(v[k].y));
+                st_nt(dst + c, make_uint4(widen_lo(v[k].x), widen_hi(v[k].x), widen_lo(v[k].y), widen_hi(v[k].y)));
         }
     }
 }
@@ -338,11 +318,11 @@ __global__ __launch_bounds__(kThreads) void selftest_codes_kernel(const uint16_t
     if (t >= cpr * ns) return;
     const int64_t i = t / cpr, j = t - i * cpr;
     const uint4 v = reinterpret_cast<const uint4*>(x)[j];
-    float s, r;
-    prep_scale(s16[i], s, r);
+    const uint32_t s = s16[i];
+    const ScaleOps so = prep_scale(s);
     uint32_t c[8];
-    if (CLAMP_ALL) quant_chunk_impl<WBITS, true>(v, s, r, c);
-    else quant_chunk<WBITS>(v, s16[i], s, r, c);
+    if (CLAMP_ALL) quant_chunk_clamped<WBITS>(v, so, c);
+    else quant_chunk<WBITS>(v, s, so, c);
     constexpr uint32_t mask = (1u << WBITS) - 1;
     uint2 o;
     o.x = (c[0] & mask) | ((c[1] & mask) << 8) | ((c[2] & mask) << 16) | ((c[3] & mask) << 24);
@@ -382,46 +362,53 @@ int launch_fp8_to_fp16(const Fp8Launch& a, void* stream) {
     return launch(reinterpret_cast<const void*>(&fp8_to_fp16_kernel), fp8_grid(a), dim3(kThreads), args, stream);
 }
 
-// Kernel variant for a call: the unguarded fast path needs every segment
-// full (row chunk count a multiple of NCH * 64).
-template <int WBITS, bool QUANT>
-static const void* q_kernel(int nch, bool guard) {
-    constexpr int U = kUnitsPerWave;
-    if (QUANT) {
-        if (guard) return reinterpret_cast<const void*>(&quant_kv_kernel<WBITS, 1, 2, true>);
-        if (nch == 2) return reinterpret_cast<const void*>(&quant_kv_kernel<WBITS, U, 2, false>);
-        return reinterpret_cast<const void*>(&quant_kv_kernel<WBITS, U, 1, false>);
-    }
-    if (guard) return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, 1, 2, true>);
-    if (nch == 2) return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, U, 2, false>);
-    return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, U, 1, false>);
+// Kernel variant for a call.  Quantize: 64 lanes x 16 elements per
+// segment, guarded when the row's 16-element pieces are not a multiple of
+// 64.  Dequantize: NCH chunks of 8 per lane, NCH = 2 (or 1) when the row's
+// chunks are a multiple of 128 (or 64), else NCH = 2 guarded.
+template <int WBITS, bool PAGED>
+static const void* quant_fn(bool guard) {
+    return guard ? reinterpret_cast<const void*>(&quant_kv_kernel<WBITS, PAGED, true>)
+                 : reinterpret_cast<const void*>(&quant_kv_kernel<WBITS, PAGED, false>);
+}
+
+template <int WBITS, bool PAGED>
+static const void* dequant_fn(int nch, bool guard) {
+    if (guard) return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, PAGED, 2, true>);
+    if (nch == 2) return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, PAGED, 2, false>);
+    return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, PAGED, 1, false>);
+}
+
+template <int WBITS>
+static const void* q_fn(bool quant, bool paged, int nch, bool guard) {
+    if (quant) return paged ? quant_fn<WBITS, true>(guard) : quant_fn<WBITS, false>(guard);
+    return paged ? dequant_fn<WBITS, true>(nch, guard) : dequant_fn<WBITS, false>(nch, guard);
 }
 
 static int launch_q(const QLaunch& a, bool quant, void* stream) {
-    const int32_t cpr = a.R >> 3;
     int nch = 2;
     bool guard = false;
-    int upw = kUnitsPerWave;
-    if (cpr % 128 == 0) {
-        nch = 2;
-    } else if (cpr % 64 == 0) {
-        nch = 1;
+    int32_t seg_elems;
+    if (quant) {
+        guard = (a.R / 16) % 64 != 0;
+        seg_elems = 1024;
     } else {
-        guard = true;
-        upw = 1;
+        const int32_t cpr = a.R >> 3;
+        if (cpr % 128 == 0) nch = 2;
+        else if (cpr % 64 == 0) nch = 1;
+        else guard = true;
+        seg_elems = nch * 64 * 8;
     }
     QGeom g;
-    g.nseg = (cpr + nch * 64 - 1) / (nch * 64);
+    g.nseg = (a.R + seg_elems - 1) / seg_elems;
     g.ntens = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
     g.tens0 = a.k_src ? 0 : 1;
     g.n_units = (int32_t)((int64_t)a.batch * a.width * g.ntens * g.nseg);   // bounded by the host checks
-    const int64_t waves = (g.n_units + upw - 1) / upw;
-    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
+    const dim3 grid((unsigned)((g.n_units + kWaves - 1) / kWaves));
     QLaunch arg = a;
     void* args[] = {&arg, &g};
-    const void* fn;
-    if (a.wbits == 4) fn = quant ? q_kernel<4, true>(nch, guard) : q_kernel<4, false>(nch, guard);
-    else fn = quant ? q_kernel<6, true>(nch, guard) : q_kernel<6, false>(nch, guard);
+    const bool paged = a.page_size != 0;
+    const void* fn = a.wbits == 4 ? q_fn<4>(quant, paged, nch, guard) : q_fn<6>(quant, paged, nch, guard);
     return launch(fn, grid, dim3(kThreads), args, stream);
 }
 
