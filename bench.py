@@ -62,28 +62,34 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-class PagedQ4:
-    """Device state of the paged Q4 workload and its two launches."""
+class PagedKV:
+    """Device state of the paged workload (4096 pages x 256 tokens, 8 heads x
+    128, 32 sequences x 256 new tokens, 32 rotated paging draws) at one code
+    width, and its two launches.  `share` reuses another instance's fp16
+    caches and paging tables."""
 
-    def __init__(self, torch, kvq, synth):
-        self.torch, self.kvq = torch, kvq
+    def __init__(self, torch, kvq, synth, wbits=4, share=None):
+        self.torch, self.kvq, self.wbits = torch, kvq, wbits
         w = synth.q4_paged(draws=DRAWS)
         self.w = w
         shape = w.shape
         t = torch
-        log("allocating paged caches %s x 2 (fp16) + codes/scales/outputs" % (shape,))
-        self.k = synth.device_normal_f16(t, shape, w.extra["device_seed"])
-        self.v = synth.device_normal_f16(t, shape, w.extra["device_seed"] + 1)
-        cs, ss = kvq.code_shape(shape, 4), kvq.scale_shape(shape)
+        if share is None:
+            log("allocating paged caches %s x 2 (fp16) + codes/scales/outputs" % (shape,))
+            self.k = synth.device_normal_f16(t, shape, w.extra["device_seed"])
+            self.v = synth.device_normal_f16(t, shape, w.extra["device_seed"] + 1)
+            self.ko = t.zeros(shape, dtype=t.float16, device="cuda")
+            self.vo = t.zeros(shape, dtype=t.float16, device="cuda")
+            self.tables = [(t.from_numpy(sl).cuda(), t.from_numpy(bt).cuda()) for sl, bt in w.extra["tables"]]
+        else:
+            self.k, self.v, self.ko, self.vo, self.tables = share.k, share.v, share.ko, share.vo, share.tables
+        cs, ss = kvq.code_shape(shape, wbits), kvq.scale_shape(shape)
         self.kq = t.zeros(cs, dtype=t.uint8, device="cuda")
         self.vq = t.zeros(cs, dtype=t.uint8, device="cuda")
         self.ks = t.zeros(ss, dtype=t.float16, device="cuda")
         self.vs = t.zeros(ss, dtype=t.float16, device="cuda")
-        self.ko = t.zeros(shape, dtype=t.float16, device="cuda")
-        self.vo = t.zeros(shape, dtype=t.float16, device="cuda")
-        self.tables = [(t.from_numpy(sl).cuda(), t.from_numpy(bt).cuda()) for sl, bt in w.extra["tables"]]
         self.rows_per_launch = 2 * w.batch_size * w.width            # K and V rows
-        self.bytes_per_launch = self.rows_per_launch * q_row_bytes(4)
+        self.bytes_per_launch = self.rows_per_launch * q_row_bytes(wbits)
         self.bytes_per_step = 2 * self.bytes_per_launch
         self.elems_per_step = 2 * self.rows_per_launch * ROW
 
@@ -91,13 +97,13 @@ class PagedQ4:
         sl, bt = self.tables[d]
         w = self.w
         self.kvq.kvq_fp16_to_q_kv(self.k, self.kq, self.ks, self.v, self.vq, self.vs, w.batch_size,
-                                  w.offset, w.width, w.page_size, sl, bt, 4)
+                                  w.offset, w.width, w.page_size, sl, bt, self.wbits)
 
     def dequant(self, d):
         sl, bt = self.tables[d]
         w = self.w
         self.kvq.kvq_q_to_fp16_kv(self.kq, self.ko, self.ks, self.vq, self.vo, self.vs, w.batch_size,
-                                  w.offset, w.width, w.page_size, sl, bt, 4)
+                                  w.offset, w.width, w.page_size, sl, bt, self.wbits)
 
     def step(self, d):
         self.quant(d)
@@ -188,7 +194,7 @@ def main():
         sys.exit(3)
     kvq.load_library()                                   # fail loudly without the HIP library
     dev_name = torch.cuda.get_device_name(0)
-    wl = PagedQ4(torch, kvq, synth)
+    wl = PagedKV(torch, kvq, synth, wbits=4)
 
     # warmup (eager), also the parity reference for graph replays
     for i in range(args.warmup):
@@ -284,7 +290,7 @@ def main():
                          "scalar C oracle, rows split over %d threads, %.2f s wall"
                          % (cb["rows"], args.cpu_draws, cb["threads"], cb["seconds"])}
 
-    secondary = None if args.no_secondary else secondary_workloads(torch, kvq, synth)
+    secondary = None if args.no_secondary else secondary_workloads(torch, kvq, synth, wl)
     if args.calibrate_copy:
         calibrate_copy(torch)
 
@@ -330,10 +336,19 @@ def sources_digest():
     return h.hexdigest()
 
 
-def secondary_workloads(torch, kvq, synth):
-    """Kernel-time GB/s of the other workloads (events around each launch)."""
+def secondary_workloads(torch, kvq, synth, wl):
+    """Kernel-time GB/s of the other widths on the paged workload (same cold
+    rotation as the headline), and of the other workloads (inputs repeated,
+    so partly cache-resident: context only)."""
     t = torch
     out = {}
+    for wb in (6, 8):
+        other = PagedKV(torch, kvq, synth, wbits=wb, share=wl)
+        kt = time_kernels(t, [("quant", other.quant, list(range(DRAWS))),
+                              ("dequant", other.dequant, list(range(DRAWS)))], 4 * DRAWS)
+        out["paged_q%d_cold" % wb] = {k: {"us": round(v * 1e6, 2), "GB/s": round(other.bytes_per_launch / v / 1e9, 1)}
+                                      for k, v in kt.items()}
+        del other
     # fp8 contiguous [1,256,8,128]
     w = synth.fp8_contig()
     x = t.from_numpy(w.k).cuda()

@@ -39,13 +39,13 @@
  * readings below are the library's definition):
  *   8-bit  byte = high byte of the fp16 pattern (e5m2, truncated toward 0);
  *          back: fp16 pattern = byte << 8.
- *   Q4/Q6  blocks of 32 consecutive elements along head_dim;
+ *   Q4/Q6/Q8  blocks of 32 consecutive elements along head_dim;
  *          s16 = fp16_rne(fp32(absmax) / (2^(b-1) - 1));
  *          q = 0 if s16 == 0, else clamp(round_half_even(x / s16),
  *              -2^(b-1), 2^(b-1) - 1); stored u = q + 2^(b-1);
  *          the codes of a row form one little-endian bit stream, code j at
  *          bits [b*j, b*j + b)  (4-bit: 8 codes per uint32 word; 6-bit: 16
- *          codes per 12 bytes).
+ *          codes per 12 bytes; 8-bit: one code per byte).
  *   dequant x' = fp16_rne((float)(u - 2^(b-1)) * (float)s16).
  *   Inputs to the quantizer must be finite; scales given to the dequantizer
  *   must be finite.  Results are bit-identical across calls and devices.
@@ -68,7 +68,7 @@ extern "C" {
 
 #define KVQ_OK            0
 #define KVQ_ERR_NULL     -1  /* a required pointer is NULL, or a K/V triple is partial */
-#define KVQ_ERR_WBITS    -2  /* wbits is not 4 or 6 */
+#define KVQ_ERR_WBITS    -2  /* wbits is not 4, 6 or 8 */
 #define KVQ_ERR_SHAPE    -3  /* heads/head_dim/dims not positive, head_dim % 32 (Q) or
                                 heads*head_dim % 8 (8-bit) not 0, paged page_size != dim1 */
 #define KVQ_ERR_RANGE    -4  /* negative size or offset, window past dim0/dim1,
@@ -109,10 +109,12 @@ KVQ_API int kvq_fp8_to_fp16(const void* in_u8, void* out_f16, kvq_shape s,
                     int batch_size, int offset, int width, void* hip_stream);
 
 /*
- * fp16 -> 4/6-bit codes and per-block fp16 scales for K and V in one launch.
- * ExLlamaV2 cache page, Description of fp16_to_q_kv (paged mode when
+ * fp16 -> 4/6/8-bit codes and per-block fp16 scales for K and V in one
+ * launch.  ExLlamaV2 cache page, Description of fp16_to_q_kv (paged mode when
  * page_size > 0, using block_table and cache_seqlens; contiguous otherwise)
- * and I/O Contract (k_scales / v_scales: per-block scale factors; wbits 4/6).
+ * and I/O Contract (k_scales / v_scales: per-block scale factors; wbits 4 or
+ * 6).  wbits 8 is the same block format with one code per byte, the width of
+ * the page's ExLlamaV2Cache_Q8 class (Usage section).
  *   k_in, v_in          device, fp16 [dim0, dim1, heads, head_dim], read
  *   k_out, v_out        device, uint8 codes [dim0, dim1, heads, head_dim*wbits/8]
  *   k_scales, v_scales  device, fp16 [dim0, dim1, heads, head_dim/32], written
@@ -137,7 +139,7 @@ KVQ_API int kvq_fp16_to_q_kv(const void* k_in, void* k_out, void* k_scales,
                      int wbits, void* hip_stream);
 
 /*
- * 4/6-bit codes + fp16 scales -> fp16 for K and V in one launch, over the
+ * 4/6/8-bit codes + fp16 scales -> fp16 for K and V in one launch, over the
  * same rows as kvq_fp16_to_q_kv with the same arguments.  ExLlamaV2 cache
  * page, Description of q_to_fp16_kv (same paged/contiguous dual path) and
  * I/O Contract (writes dequantized FP16 values into k_out / v_out).

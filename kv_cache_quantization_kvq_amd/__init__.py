@@ -190,8 +190,8 @@ def _q_common(quant, k_in, k_out, k_scales, v_in, v_out, v_scales, batch_size, o
         raise ValueError("%s: at least one of the K and V triples is required" % fname)
     shp = _shape4(ref, "cache")
     dev = ref.device
-    if wbits not in (4, 6):
-        raise ValueError("wbits must be 4 or 6")
+    if wbits not in (4, 6, 8):
+        raise ValueError("wbits must be 4, 6 or 8")
     cshape, sshape = code_shape(shp, wbits), scale_shape(shp)
     src_t, dst_t = (torch.float16, torch.uint8) if quant else (torch.uint8, torch.float16)
     src_s, dst_s = (shp, cshape) if quant else (cshape, shp)

@@ -90,7 +90,7 @@ int q_call(bool quant, const void* k_src, void* k_dst, const void* k_scales, con
            void* v_dst, const void* v_scales, kvq_shape s, int batch_size, int offset, int width,
            int page_size, const int32_t* cache_seqlens, const int32_t* block_table,
            int block_table_cols, int wbits, void* stream) {
-    if (wbits != 4 && wbits != 6) return KVQ_ERR_WBITS;
+    if (wbits != 4 && wbits != 6 && wbits != 8) return KVQ_ERR_WBITS;
     const bool k_any = k_src || k_dst || k_scales, k_all = k_src && k_dst && k_scales;
     const bool v_any = v_src || v_dst || v_scales, v_all = v_src && v_dst && v_scales;
     if ((k_any && !k_all) || (v_any && !v_all) || (!k_any && !v_any)) return KVQ_ERR_NULL;
@@ -210,7 +210,7 @@ const char* kvq_strerror(int code) {
     switch (code) {
         case KVQ_OK: return "success";
         case KVQ_ERR_NULL: return "required pointer is NULL or a K/V triple is partial";
-        case KVQ_ERR_WBITS: return "wbits must be 4 or 6";
+        case KVQ_ERR_WBITS: return "wbits must be 4, 6 or 8";
         case KVQ_ERR_SHAPE: return "invalid cache shape (head_dim % 32 for Q paths, heads*head_dim % 8 for 8-bit, page_size == dim1 when paged)";
         case KVQ_ERR_RANGE: return "size, offset or window out of range";
         case KVQ_ERR_ALIGN: return "device pointer not 16-byte aligned (int32 tables: 4)";
@@ -224,7 +224,7 @@ int kvq_version(void) { return 100; }
 
 int kvq_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s16, int64_t ns, int wbits,
                        int force_clamp, uint8_t* u_out, void* hip_stream) {
-    if (wbits != 4 && wbits != 6) return KVQ_ERR_WBITS;
+    if (wbits != 4 && wbits != 6 && wbits != 8) return KVQ_ERR_WBITS;
     if (!x || !s16 || !u_out) return KVQ_ERR_NULL;
     if (nx < 0 || ns < 0 || nx % 8 != 0) return KVQ_ERR_RANGE;
     if (!aligned(x, 16) || !aligned(u_out, 16) || !aligned(s16, 2)) return KVQ_ERR_ALIGN;
@@ -235,7 +235,7 @@ int kvq_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s16, int64
 }
 
 int kvq_selftest_scales(const uint16_t* absmax, int64_t n, int wbits, uint16_t* out, void* hip_stream) {
-    if (wbits != 4 && wbits != 6) return KVQ_ERR_WBITS;
+    if (wbits != 4 && wbits != 6 && wbits != 8) return KVQ_ERR_WBITS;
     if (!absmax || !out) return KVQ_ERR_NULL;
     if (n < 0 || n > (int64_t)INT32_MAX * 64) return KVQ_ERR_RANGE;
     if (!aligned(absmax, 2) || !aligned(out, 2)) return KVQ_ERR_ALIGN;

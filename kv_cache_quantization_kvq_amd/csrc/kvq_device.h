@@ -254,6 +254,14 @@ __device__ __forceinline__ void pack_q6(const uint32_t (&u)[8], uint32_t& lo, ui
     hi = (u[5] >> 2) | (u[6] << 4) | (u[7] << 10);
 }
 
+// 8-bit block codes: code j is byte j; four codes per word, assembled with
+// byte permutes from the low bytes of the element results.
+__device__ __forceinline__ uint32_t pack_q8x4(uint32_t u0, uint32_t u1, uint32_t u2, uint32_t u3) {
+    const uint32_t t01 = __builtin_amdgcn_perm(u1, u0, 0x00000400u);   // [u0.b0, u1.b0, -, -]
+    const uint32_t t23 = __builtin_amdgcn_perm(u3, u2, 0x00000400u);   // [u2.b0, u3.b0, -, -]
+    return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+}
+
 // ---------------------------------------------------------------- dequantize
 //
 // Codes become exact fp16 integers through the bit pattern 0x6400 | u
@@ -298,6 +306,24 @@ __device__ __forceinline__ uint4 dequant_q6_chunk(uint32_t lo, uint32_t hi, uint
     o.y = as_u32(q6_pair(lo >> 12) * s);
     o.z = as_u32(q6_pair(__builtin_amdgcn_alignbit(hi, lo, 24)) * s);
     o.w = as_u32(q6_pair(hi >> 4) * s);
+    return o;
+}
+
+// Pair of 8-bit codes (bytes SEL0, SEL1 of w) -> fp16 (1024 + u) in each
+// half: the byte permute fills the high byte of each half with 0x64.
+__device__ __forceinline__ half2_t q8_pair(uint32_t w, uint32_t sel) {
+    const uint32_t t = __builtin_amdgcn_perm(0x64646464u, w, sel);
+    const half2_t off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    return as_h2(t) + off;
+}
+
+__device__ __forceinline__ uint4 dequant_q8_chunk(uint32_t lo, uint32_t hi, uint32_t s2) {
+    const half2_t s = as_h2(s2);
+    uint4 o;
+    o.x = as_u32(q8_pair(lo, 0x04010400u) * s);
+    o.y = as_u32(q8_pair(lo, 0x04030402u) * s);
+    o.z = as_u32(q8_pair(hi, 0x04010400u) * s);
+    o.w = as_u32(q8_pair(hi, 0x04030402u) * s);
     return o;
 }
 

@@ -156,6 +156,10 @@ __global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, QGeom g) 
     if constexpr (WBITS == 4) {
         const uint2 d = make_uint2(pack_q4(u0), pack_q4(u1));
         if (store) *reinterpret_cast<uint2*>(codes + 8 * pc) = d;
+    } else if constexpr (WBITS == 8) {
+        const uint4 d = make_uint4(pack_q8x4(u0[0], u0[1], u0[2], u0[3]), pack_q8x4(u0[4], u0[5], u0[6], u0[7]),
+                                   pack_q8x4(u1[0], u1[1], u1[2], u1[3]), pack_q8x4(u1[4], u1[5], u1[6], u1[7]));
+        if (store) *reinterpret_cast<uint4*>(codes + 16 * pc) = d;
     } else {
         uint32_t lo0, hi0, lo1, hi1;
         pack_q6(u0, lo0, hi0);
@@ -188,6 +192,10 @@ __device__ __forceinline__ CodeChunk load_code_chunk(const uint8_t* __restrict__
     if constexpr (WBITS == 4) {
         q.lo = ld_nt(reinterpret_cast<const uint32_t*>(codes_row) + c);
         q.hi = 0;
+    } else if constexpr (WBITS == 8) {
+        const uint32_t* g = reinterpret_cast<const uint32_t*>(codes_row) + 2 * c;
+        q.lo = ld_nt(g);
+        q.hi = ld_nt(g + 1);
     } else {
         // chunk c's 6 bytes start at 6c: load the 8 bytes of its 12-byte
         // group that contain them (4-byte aligned); odd chunks are shifted
@@ -205,6 +213,8 @@ __device__ __forceinline__ uint4 dequant_chunk(const CodeChunk& q, int32_t c) {
     const uint32_t s2 = q.s | (q.s << 16);
     if constexpr (WBITS == 4) {
         return dequant_q4_chunk(q.lo, s2);
+    } else if constexpr (WBITS == 8) {
+        return dequant_q8_chunk(q.lo, q.hi, s2);
     } else {
         uint32_t lo, hi;
         if (c & 1) {
@@ -408,7 +418,9 @@ static int launch_q(const QLaunch& a, bool quant, void* stream) {
     QLaunch arg = a;
     void* args[] = {&arg, &g};
     const bool paged = a.page_size != 0;
-    const void* fn = a.wbits == 4 ? q_fn<4>(quant, paged, nch, guard) : q_fn<6>(quant, paged, nch, guard);
+    const void* fn = a.wbits == 4 ? q_fn<4>(quant, paged, nch, guard)
+                   : a.wbits == 6 ? q_fn<6>(quant, paged, nch, guard)
+                                  : q_fn<8>(quant, paged, nch, guard);
     return launch(fn, grid, dim3(kThreads), args, stream);
 }
 
@@ -425,9 +437,12 @@ int launch_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s, int6
     if (wbits == 4)
         fn = force_clamp ? reinterpret_cast<const void*>(&selftest_codes_kernel<4, true>)
                          : reinterpret_cast<const void*>(&selftest_codes_kernel<4, false>);
-    else
+    else if (wbits == 6)
         fn = force_clamp ? reinterpret_cast<const void*>(&selftest_codes_kernel<6, true>)
                          : reinterpret_cast<const void*>(&selftest_codes_kernel<6, false>);
+    else
+        fn = force_clamp ? reinterpret_cast<const void*>(&selftest_codes_kernel<8, true>)
+                         : reinterpret_cast<const void*>(&selftest_codes_kernel<8, false>);
     return launch(fn, grid, dim3(kThreads), args, stream);
 }
 
@@ -435,7 +450,8 @@ int launch_selftest_scales(const uint16_t* a, int64_t n, int wbits, uint16_t* ou
     dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
     void* args[] = {&a, &n, &out};
     const void* fn = wbits == 4 ? reinterpret_cast<const void*>(&selftest_scales_kernel<4>)
-                                : reinterpret_cast<const void*>(&selftest_scales_kernel<6>);
+                   : wbits == 6 ? reinterpret_cast<const void*>(&selftest_scales_kernel<6>)
+                                : reinterpret_cast<const void*>(&selftest_scales_kernel<8>);
     return launch(fn, grid, dim3(kThreads), args, stream);
 }
 

@@ -79,7 +79,8 @@ def q(lib, quant=True, k=(A, A + GB, A + 2 * GB), v=(A + 3 * GB, A + 4 * GB, A +
 
 def test_q_validation(lib):
     assert q(lib, wbits=5) == WBITS
-    assert q(lib, wbits=8) == WBITS
+    assert q(lib, wbits=7) == WBITS
+    assert q(lib, wbits=16) == WBITS
     assert q(lib, k=(A, None, A + 2 * GB)) == NULL                       # partial triple
     assert q(lib, k=(None, None, None), v=(None, None, None)) == NULL
     assert q(lib, s=shp(d=48)) == SHAPE                                    # head_dim % 32
@@ -105,6 +106,7 @@ def test_q_zero_work_returns_ok(lib):
     # valid arguments but nothing to do: no launch, success
     assert q(lib, width=0) == 0
     assert q(lib, batch=0) == 0
+    assert q(lib, width=0, wbits=8) == 0 and q(lib, quant=False, width=0, wbits=6) == 0
     assert q(lib, k=(None, None, None), width=0) == 0
     assert q(lib, page_size=16, sl=A + 6 * GB, bt=A + 7 * GB, cols=4, batch=0) == 0
     # paged mode allows batch_size > dim0 (sequences are not pages)

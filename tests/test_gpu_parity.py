@@ -43,7 +43,7 @@ def _ss(shape):
 
 
 # ---------------------------------------------------------------- element-level sweeps
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_scale_rule_exhaustive(kvq, wbits):
     """Device scale rule on every finite fp16 absmax vs the oracle's fp32
     divide + fp16 rounding."""
@@ -54,7 +54,7 @@ def test_scale_rule_exhaustive(kvq, wbits):
     byte_diff(host(out).view(np.uint16), oracle.scale_from_absmax(a, wbits), "scales")
 
 
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_code_rule_exhaustive(kvq, wbits):
     """Device element code on every finite fp16 x under every finite fp16
     scale >= 0 (including 0 and subnormals) vs the oracle: 63488 x 31744
@@ -91,7 +91,7 @@ def test_code_rule_exhaustive(kvq, wbits):
     pool.shutdown()
 
 
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_dequant_exhaustive_through_kernel(kvq, wbits):
     """Every (code, scale) pair for all finite scales >= 0 through the
     production dequant kernel: block i carries scale i, codes cycle."""
@@ -101,7 +101,7 @@ def test_dequant_exhaustive_through_kernel(kvq, wbits):
     R = 1024
     rows = nblk * 32 // R                                # 992 rows
     shape = (1, rows, 1, R)
-    for phase in (0, 32):
+    for phase in range(0, 1 << wbits, 32):
         u = (np.arange(nblk * 32) + phase) % (1 << wbits)
         codes = oracle.pack_bits(u.astype(np.uint8), wbits).reshape(_cs(shape, wbits))
         sc = scales.reshape(_ss(shape)).copy()
@@ -145,6 +145,12 @@ def test_q4_contig_workload(kvq):
     _contig_roundtrip(kvq, w.k, w.v, w.batch_size, w.offset, w.width, 4, what="q4_contig")
 
 
+def test_q8_contig_window(kvq):
+    """Block Q8 (one code per byte) on the outlier workload's caches and window."""
+    w = synth.q4_contig()
+    _contig_roundtrip(kvq, w.k, w.v, w.batch_size, w.offset, w.width, 8, what="q8_contig")
+
+
 def test_q6_contig_workload(kvq):
     w = synth.q6_contig()
     _log("q6_contig %s" % (w.shape,))
@@ -153,7 +159,7 @@ def test_q6_contig_workload(kvq):
 
 @pytest.mark.parametrize("heads,head_dim", [(1, 32), (3, 32), (1, 96), (5, 32), (2, 64),
                                              (8, 128), (3, 1376), (1, 2080)])
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_contig_ragged_shapes(kvq, heads, head_dim, wbits):
     """Rows of 32..4128 elements: partial waves, several segments per row,
     ragged batch / window."""
@@ -171,7 +177,7 @@ ALPHABET = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x0003, 0x000A, 0x03FF, 0x0
                      0x3555, 0x7BFF, 0xFBFF, 0x1234, 0x2E66, 0x4B80], np.uint16)
 
 
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_edge_value_blocks(kvq, wbits):
     """Blocks drawn from zeros of both signs, subnormals, tie makers and
     +-65504, plus all-zero blocks and blocks whose scale underflows."""
@@ -198,7 +204,7 @@ def test_k_only_and_v_only(kvq):
     rng = np.random.default_rng(5)
     shape = (2, 16, 2, 64)
     x = (rng.standard_normal(shape)).astype(np.float16)
-    for wbits in (4, 6):
+    for wbits in (4, 6, 8):
         codes = sentinel(_cs(shape, wbits), t.uint8)
         sc = sentinel(_ss(shape), t.float16)
         kvq.kvq_fp16_to_q_kv(None, None, None, dev(x), codes, sc, 2, 3, 5, wbits=wbits)
@@ -269,7 +275,7 @@ def _paged_roundtrip_small(kvq, shape, batch, offset, width, sl, bt, wbits, seed
 
 
 @pytest.mark.parametrize("page_size", [1, 3, 16])
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_paged_small_with_invalid_entries(kvq, page_size, wbits):
     """Tiny pages, tables with -1 / out-of-range pages, negative and
     past-the-table positions: those rows are skipped on both sides."""

@@ -26,7 +26,7 @@ def QZ(wbits):
 
 
 # ---------------------------------------------------------------- scale
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_scale_equals_exact_rational_rounding(wbits):
     """fp32 divide then fp16 rounding == single correct rounding of the exact
     rational a/Q, for every finite fp16 absmax."""
@@ -37,7 +37,7 @@ def test_scale_equals_exact_rational_rounding(wbits):
     assert (got == want).all()
 
 
-@pytest.mark.parametrize("wbits,n_zero,n_sub", [(4, 3, 3836), (6, 15, 6064)])
+@pytest.mark.parametrize("wbits,n_zero,n_sub", [(4, 3, 3836), (6, 15, 6064), (8, 63, 8112)])
 def test_scale_underflow_counts(wbits, n_zero, n_sub):
     s = oracle.scale_from_absmax(POS_FINITE, wbits)
     assert int(((s == 0) & (POS_FINITE != 0)).sum()) == n_zero
@@ -45,7 +45,7 @@ def test_scale_underflow_counts(wbits, n_zero, n_sub):
 
 
 # ---------------------------------------------------------------- codes
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_normal_scale_never_needs_the_clamp(wbits):
     """For every finite absmax a whose stored scale s16 is a normal fp16,
     a / s16 < Q + 1/2 exactly: every element of such a block rounds into
@@ -67,7 +67,7 @@ def _scale_sample():
     return s[pick]
 
 
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_codes_exact_integer_rounding(wbits):
     """For all finite fp16 x and a wide sample of positive fp16 scales, the
     oracle's fp32 path equals integer round-half-even of X/S, clamped."""
@@ -80,7 +80,7 @@ def test_codes_exact_integer_rounding(wbits):
         assert (u == want).all(), hex(int(s))
 
 
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_codes_bruteforce_argmin(wbits):
     """Nearest representable multiple k*s, k in [-Z, Z-1], ties to even k, on
     every finite x for a handful of scales, including ones with exact ties."""
@@ -94,14 +94,14 @@ def test_codes_bruteforce_argmin(wbits):
 
 
 def test_zero_scale_gives_zero_code():
-    for wbits in (4, 6):
+    for wbits in (4, 6, 8):
         _, Z = QZ(wbits)
         u = oracle.quant_elems(ALL_FINITE, 0, wbits)
         assert (u == Z).all()
 
 
 # ---------------------------------------------------------------- dequant
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_dequant_exhaustive_vs_numpy(wbits):
     _, Z = QZ(wbits)
     u = np.arange(1 << wbits, dtype=np.uint8)
@@ -145,7 +145,7 @@ def test_pack_golden_vectors():
         assert oracle.unpack_bits(np.frombuffer(want, np.uint8), len(codes), wbits).tolist() == codes
 
 
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_pack_equals_big_integer(wbits):
     """The stream equals the little-endian bytes of sum_j u_j * 2^(b*j)."""
     rng = np.random.default_rng(11)
@@ -192,7 +192,7 @@ def _round_trip_ok(x_bits, s16, u, xq_bits, wbits):
     return ok.all()
 
 
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_block_invariants_random(wbits):
     Q, Z = QZ(wbits)
     rng = np.random.default_rng(5 + wbits)
@@ -224,7 +224,7 @@ ALPHABET = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x0003, 0x000A, 0x03FF, 0x0
                     np.uint16)
 
 
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_tiny_blocks_bruteforce(wbits):
     """Every block of length 1..3 over a 24-value alphabet (zeros of both signs,
     subnormals, values that make exact ties, +-65504): scale = correctly rounded
@@ -253,7 +253,7 @@ def test_clamp_example_subnormal_scale():
 
 
 # ---------------------------------------------------------------- rows
-@pytest.mark.parametrize("wbits", [4, 6])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_rows_compose_blocks_and_stream(wbits):
     """A token row is its 32-element blocks quantized independently, scales in
     block order, and all codes of the row in one bit stream."""
