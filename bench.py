@@ -336,12 +336,21 @@ def sources_digest():
     return h.hexdigest()
 
 
+def fmt_row_bytes(fmt):
+    """Algorithmic bytes per token row, either direction, for a per-tensor
+    format (0 = 8-bit high byte)."""
+    return ROW * 2 + ROW if fmt == 0 else q_row_bytes(fmt)
+
+
 def secondary_workloads(torch, kvq, synth, wl):
-    """Kernel-time GB/s of the other widths on the paged workload (same cold
-    rotation as the headline), and of the other workloads (inputs repeated,
-    so partly cache-resident: context only)."""
+    """Kernel-time GB/s of the other paths, each with cold inputs (rotated
+    paging draws) unless labelled hot (inputs repeated, partly
+    cache-resident: context only)."""
     t = torch
     out = {}
+    w = wl.w
+    rows = w.batch_size * w.width
+    # other block widths on the paged workload
     for wb in (6, 8):
         other = PagedKV(torch, kvq, synth, wbits=wb, share=wl)
         kt = time_kernels(t, [("quant", other.quant, list(range(DRAWS))),
@@ -349,51 +358,85 @@ def secondary_workloads(torch, kvq, synth, wl):
         out["paged_q%d_cold" % wb] = {k: {"us": round(v * 1e6, 2), "GB/s": round(other.bytes_per_launch / v / 1e9, 1)}
                                       for k, v in kt.items()}
         del other
-    # fp8 contiguous [1,256,8,128]
-    w = synth.fp8_contig()
-    x = t.from_numpy(w.k).cuda()
-    o8 = t.empty(w.shape, dtype=t.uint8, device="cuda")
-    ob = t.empty(w.shape, dtype=t.float16, device="cuda")
+    # paged 8-bit (high byte) through the per-tensor entry points
+    kc = t.zeros(w.shape, dtype=t.uint8, device="cuda")
+    vc = t.zeros(w.shape, dtype=t.uint8, device="cuda")
+
+    def narrow(d):
+        sl, bt = wl.tables[d]
+        kvq.kvq_fp16_to_kv(wl.k, kc, None, 0, wl.v, vc, None, 0, w.batch_size, w.offset, w.width, w.page_size, sl, bt)
+
+    def widen(d):
+        sl, bt = wl.tables[d]
+        kvq.kvq_kv_to_fp16(kc, wl.ko, None, 0, vc, wl.vo, None, 0, w.batch_size, w.offset, w.width, w.page_size, sl, bt)
+
+    kt = time_kernels(t, [("fp16_to_8bit", narrow, list(range(DRAWS))), ("8bit_to_fp16", widen, list(range(DRAWS)))],
+                      4 * DRAWS)
+    nb = 2 * rows * fmt_row_bytes(0)
+    out["paged_fp8_cold"] = {k: {"us": round(v * 1e6, 2), "GB/s": round(nb / v / 1e9, 1)} for k, v in kt.items()}
+    del kc, vc
+    # full-prefix widen of the Q4 caches: positions [0, cache_seqlens[b] + width)
+    max_len = w.block_table.shape[1] * w.page_size
+    pbytes = [2 * int(np.minimum(sl.astype(np.int64) + w.width, max_len).sum()) * q_row_bytes(4)
+              for sl, _ in w.extra["tables"]]
+
+    def prefix(d):
+        sl, bt = wl.tables[d]
+        kvq.kvq_kv_to_fp16_prefix(wl.kq, wl.ko, wl.ks, 4, wl.vq, wl.vo, wl.vs, 4, w.batch_size, w.width, max_len, sl, bt)
+
+    kt = time_kernels(t, [("prefix", prefix, list(range(DRAWS)))], 2 * DRAWS)
+    out["prefix_widen_q4_cold"] = {"us": round(kt["prefix"] * 1e6, 2), "MB": round(np.mean(pbytes) / 1e6, 1),
+                                   "GB/s": round(np.mean(pbytes) / kt["prefix"] / 1e9, 1)}
+    # contiguous workloads (hot)
+    x = t.from_numpy(synth.fp8_contig().k).cuda()
+    o8 = t.empty(x.shape, dtype=t.uint8, device="cuda")
+    ob = t.empty(x.shape, dtype=t.float16, device="cuda")
     kt = time_kernels(t, [("to_fp8", lambda _: kvq.kvq_fp16_to_fp8(x, o8, 1, 0, 256), [0]),
                           ("to_fp16", lambda _: kvq.kvq_fp8_to_fp16(o8, ob, 1, 0, 256), [0])], 64)
     nb = 256 * ROW * 3
-    out["fp8_contig"] = {k: {"us": round(v * 1e6, 2), "GB/s": round(nb / v / 1e9, 1)} for k, v in kt.items()}
-    # Q4 contiguous window, Q6 contiguous
-    for name, fn, wb in (("q4_contig", synth.q4_contig, 4), ("q6_contig", synth.q6_contig, 6)):
-        w = fn()
-        k, v = t.from_numpy(w.k).cuda(), t.from_numpy(w.v).cuda()
-        cs, ss = kvq.code_shape(w.shape, wb), kvq.scale_shape(w.shape)
+    out["fp8_contig_hot"] = {k: {"us": round(v * 1e6, 2), "GB/s": round(nb / v / 1e9, 1)} for k, v in kt.items()}
+    for name, fn, wb in (("q4_contig_hot", synth.q4_contig, 4), ("q6_contig_hot", synth.q6_contig, 6)):
+        cw = fn()
+        k, v = t.from_numpy(cw.k).cuda(), t.from_numpy(cw.v).cuda()
+        cs, ss = kvq.code_shape(cw.shape, wb), kvq.scale_shape(cw.shape)
         kq, vq = t.empty(cs, dtype=t.uint8, device="cuda"), t.empty(cs, dtype=t.uint8, device="cuda")
         ks, vs = t.empty(ss, dtype=t.float16, device="cuda"), t.empty(ss, dtype=t.float16, device="cuda")
         ko, vo = t.empty_like(k), t.empty_like(v)
-        a = (w.batch_size, w.offset, w.width)
+        a = (cw.batch_size, cw.offset, cw.width)
         kt = time_kernels(t, [
             ("quant", lambda _: kvq.kvq_fp16_to_q_kv(k, kq, ks, v, vq, vs, *a, wbits=wb), [0]),
             ("dequant", lambda _: kvq.kvq_q_to_fp16_kv(kq, ko, ks, vq, vo, vs, *a, wbits=wb), [0])], 32)
-        nb = 2 * w.batch_size * w.width * q_row_bytes(wb)
+        nb = 2 * cw.batch_size * cw.width * q_row_bytes(wb)
         out[name] = {kk: {"us": round(vv * 1e6, 2), "GB/s": round(nb / vv / 1e9, 1)} for kk, vv in kt.items()}
         del k, v, kq, vq, ks, vs, ko, vo
-    # paged K-Q4 + V-Q6 at 16384 pages (8 GiB per fp16 cache)
-    w = synth.mix_paged()
-    shape = w.shape
-    k = synth.device_normal_f16(t, shape, w.extra["device_seed"])
-    v = synth.device_normal_f16(t, shape, w.extra["device_seed"] + 1)
-    kq = t.empty(kvq.code_shape(shape, 4), dtype=t.uint8, device="cuda")
-    vq = t.empty(kvq.code_shape(shape, 6), dtype=t.uint8, device="cuda")
-    ks = t.empty(kvq.scale_shape(shape), dtype=t.float16, device="cuda")
-    vs = t.empty(kvq.scale_shape(shape), dtype=t.float16, device="cuda")
+    # large paged K-Q4 + V-Q6 (8 GiB per fp16 cache), 8 rotated draws:
+    # two single-width launches per direction vs one per-tensor launch
+    mw = synth.mix_paged(draws=8)
+    shape = mw.shape
+    k = synth.device_normal_f16(t, shape, mw.extra["device_seed"])
+    v = synth.device_normal_f16(t, shape, mw.extra["device_seed"] + 1)
+    kq = t.zeros(kvq.code_shape(shape, 4), dtype=t.uint8, device="cuda")
+    vq = t.zeros(kvq.code_shape(shape, 6), dtype=t.uint8, device="cuda")
+    ks = t.zeros(kvq.scale_shape(shape), dtype=t.float16, device="cuda")
+    vs = t.zeros(kvq.scale_shape(shape), dtype=t.float16, device="cuda")
     ko, vo = t.empty_like(k), t.empty_like(v)
-    sl, bt = t.from_numpy(w.cache_seqlens).cuda(), t.from_numpy(w.block_table).cuda()
-    a = (w.batch_size, w.offset, w.width, w.page_size, sl, bt)
+    tabs = [(t.from_numpy(sl).cuda(), t.from_numpy(bt).cuda()) for sl, bt in mw.extra["tables"]]
+    nd = len(tabs)
+
+    def ar(d):
+        return (mw.batch_size, mw.offset, mw.width, mw.page_size) + tabs[d]
+
     kt = time_kernels(t, [
-        ("quant_k4", lambda _: kvq.kvq_fp16_to_q_kv(k, kq, ks, None, None, None, *a, 4), [0]),
-        ("quant_v6", lambda _: kvq.kvq_fp16_to_q_kv(None, None, None, v, vq, vs, *a, 6), [0]),
-        ("dequant_k4", lambda _: kvq.kvq_q_to_fp16_kv(kq, ko, ks, None, None, None, *a, 4), [0]),
-        ("dequant_v6", lambda _: kvq.kvq_q_to_fp16_kv(None, None, None, vq, vo, vs, *a, 6), [0])], 32)
-    rows = w.batch_size * w.width
-    nbs = {"quant_k4": rows * q_row_bytes(4), "dequant_k4": rows * q_row_bytes(4),
-           "quant_v6": rows * q_row_bytes(6), "dequant_v6": rows * q_row_bytes(6)}
-    out["mix_paged"] = {kk: {"us": round(vv * 1e6, 2), "GB/s": round(nbs[kk] / vv / 1e9, 1)} for kk, vv in kt.items()}
+        ("quant_k4_then_v6", lambda d: (kvq.kvq_fp16_to_q_kv(k, kq, ks, None, None, None, *ar(d), 4),
+                                        kvq.kvq_fp16_to_q_kv(None, None, None, v, vq, vs, *ar(d), 6)), list(range(nd))),
+        ("dequant_k4_then_v6", lambda d: (kvq.kvq_q_to_fp16_kv(kq, ko, ks, None, None, None, *ar(d), 4),
+                                          kvq.kvq_q_to_fp16_kv(None, None, None, vq, vo, vs, *ar(d), 6)), list(range(nd))),
+        ("quant_one_launch", lambda d: kvq.kvq_fp16_to_kv(k, kq, ks, 4, v, vq, vs, 6, *ar(d)), list(range(nd))),
+        ("dequant_one_launch", lambda d: kvq.kvq_kv_to_fp16(kq, ko, ks, 4, vq, vo, vs, 6, *ar(d)), list(range(nd)))],
+        4 * nd)
+    nb = mw.batch_size * mw.width * (q_row_bytes(4) + q_row_bytes(6))
+    out["mix_paged_cold"] = {kk: {"us": round(vv * 1e6, 2), "GB/s": round(nb / vv / 1e9, 1)} for kk, vv in kt.items()}
+    del k, v, kq, vq, ks, vs, ko, vo
     # a plain device copy moving the same bytes as one paged-Q4 launch
     # (read half, write half): the practical bandwidth at this launch size
     n = 2 * 32 * 256 * q_row_bytes(4) // 2 // 2
@@ -402,14 +445,13 @@ def secondary_workloads(torch, kvq, synth, wl):
     kt = time_kernels(t, [("copy", lambda d: dst[d].copy_(src[d]), list(range(DRAWS)))], 4 * DRAWS)
     out["copy_same_bytes"] = {"us": round(kt["copy"] * 1e6, 2), "GB/s": round(4 * n / kt["copy"] / 1e9, 1)}
     del src, dst
-    ids_a, ids_b = w.extra["ids_a"], w.extra["ids_b"]
+    ids_a, ids_b = mw.extra["ids_a"], mw.extra["ids_b"]
     reps = 200
     t0 = time.perf_counter()
     for _ in range(reps):
         m = kvq.kvq_count_match(ids_a, ids_b, ids_a.size)
     dt = (time.perf_counter() - t0) / reps
     out["count_match"] = {"us": round(dt * 1e6, 2), "match": m, "n": int(ids_a.size)}
-    del k, v, kq, vq, ks, vs, ko, vo
     torch.cuda.empty_cache()
     return out
 

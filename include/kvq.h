@@ -68,7 +68,7 @@ extern "C" {
 
 #define KVQ_OK            0
 #define KVQ_ERR_NULL     -1  /* a required pointer is NULL, or a K/V triple is partial */
-#define KVQ_ERR_WBITS    -2  /* wbits is not 4, 6 or 8 */
+#define KVQ_ERR_WBITS    -2  /* wbits not 4, 6 or 8 (or an unknown KVQ_FMT_* format) */
 #define KVQ_ERR_SHAPE    -3  /* heads/head_dim/dims not positive, head_dim % 32 (Q) or
                                 heads*head_dim % 8 (8-bit) not 0, paged page_size != dim1 */
 #define KVQ_ERR_RANGE    -4  /* negative size or offset, window past dim0/dim1,
@@ -165,6 +165,68 @@ KVQ_API int kvq_q_to_fp16_kv(const void* k_in, void* k_out, const void* k_scales
  */
 KVQ_API int64_t kvq_count_match(const void* a, int64_t len_a, const void* b, int64_t len_b,
                         int64_t max_a, int elem_bytes);
+
+/* ------------------------------------------------------------------------
+ * Per-tensor formats.  The page's K/V functions take one wbits for both
+ * tensors and its 8-bit functions have no paging arguments; the entry points
+ * below take a format per tensor, so K and V may differ (one launch) and the
+ * 8-bit format can be paged.  A tensor is present when its input and output
+ * pointers are non-NULL (both, or neither); its scales pointer must be
+ * non-NULL for the block formats and NULL for KVQ_FMT_FP8.  Shapes, rows,
+ * paging and skipping are those of kvq_fp16_to_q_kv; head_dim % 32 == 0.
+ * A format outside {FP8, Q4, Q6, Q8} is KVQ_ERR_WBITS.
+ *   FP8 tensor: [dim0, dim1, heads, head_dim] uint8, no scales.
+ *   Qb tensor:  codes [dim0, dim1, heads, head_dim*b/8] uint8 + fp16 scales
+ *               [dim0, dim1, heads, head_dim/32].
+ * ------------------------------------------------------------------------ */
+#define KVQ_FMT_FP8    0   /* 8-bit: high byte of the fp16 pattern */
+#define KVQ_FMT_Q4     4   /* 4-bit block codes + fp16 scale per 32 elements */
+#define KVQ_FMT_Q6     6
+#define KVQ_FMT_Q8     8
+#define KVQ_FMT_FP16  16   /* uncompressed fp16 (capacity helper only) */
+
+/* fp16 -> per-tensor formats for K and V in one launch (ExLlamaV2 cache
+ * page, Description of fp16_to_fp8 and fp16_to_q_kv, generalised). */
+KVQ_API int kvq_fp16_to_kv(const void* k_in, void* k_out, void* k_scales, int fmt_k,
+                           const void* v_in, void* v_out, void* v_scales, int fmt_v,
+                           kvq_shape s, int batch_size, int offset, int width,
+                           int page_size, const int32_t* cache_seqlens,
+                           const int32_t* block_table, int block_table_cols,
+                           void* hip_stream);
+
+/* Per-tensor formats -> fp16 for K and V in one launch, over the same rows
+ * (ExLlamaV2 cache page, Description of fp8_to_fp16 and q_to_fp16_kv,
+ * generalised).  k_in / v_in are the compact caches, k_out / v_out fp16. */
+KVQ_API int kvq_kv_to_fp16(const void* k_in, void* k_out, const void* k_scales, int fmt_k,
+                           const void* v_in, void* v_out, const void* v_scales, int fmt_v,
+                           kvq_shape s, int batch_size, int offset, int width,
+                           int page_size, const int32_t* cache_seqlens,
+                           const int32_t* block_table, int block_table_cols,
+                           void* hip_stream);
+
+/* Full-prefix widen of a paged cache: for every sequence b < batch_size,
+ * positions p in [0, min(cache_seqlens[b] + width, max_len)) -- the cached
+ * tokens plus `width` just appended, i.e. everything attention reads (the
+ * page's Usage section: the cache classes convert during the attention
+ * forward pass) -- are converted from the compact caches into the fp16
+ * caches at the same physical rows.  Paged only: page_size = dim1; p lives in
+ * page block_table[b * block_table_cols + p / dim1], slot p % dim1; positions
+ * past the table or with a page outside [0, dim0) are skipped.  max_len
+ * bounds the launch (e.g. block_table_cols * dim1); batch_size * max_len rows
+ * are enumerated.  Formats and pointers as kvq_kv_to_fp16. */
+KVQ_API int kvq_kv_to_fp16_prefix(const void* k_in, void* k_out, const void* k_scales, int fmt_k,
+                                  const void* v_in, void* v_out, const void* v_scales, int fmt_v,
+                                  kvq_shape s, int batch_size, int width, int max_len,
+                                  const int32_t* cache_seqlens, const int32_t* block_table,
+                                  int block_table_cols, void* hip_stream);
+
+/* Bytes one token occupies in one cache tensor (K or V) of a format:
+ * KVQ_FMT_FP16 2R, KVQ_FMT_FP8 R, Qb R*b/8 + 2*R/32, with R = heads*head_dim
+ * -- the capacity arithmetic a planner needs (the unsloth planning page
+ * sizes the KV cache per context length and cache type).  Host only.
+ * Returns KVQ_ERR_WBITS for an unknown format, KVQ_ERR_SHAPE for
+ * non-positive sizes or head_dim % 32 != 0 with a block format. */
+KVQ_API int64_t kvq_bytes_per_token(int format, int heads, int head_dim);
 
 /* Static description of a KVQ_* code ("unknown error" for anything else). */
 KVQ_API const char* kvq_strerror(int code);

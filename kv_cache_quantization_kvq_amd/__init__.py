@@ -22,7 +22,12 @@ from . import _build
 __all__ = ["KvqError", "kvq_fp16_to_fp8", "kvq_fp8_to_fp16", "kvq_fp16_to_q_kv",
            "kvq_q_to_fp16_kv", "kvq_count_match", "kvq_strerror", "kvq_version",
            "kvq_selftest_codes", "kvq_selftest_scales", "library_path", "load_library",
-           "code_shape", "scale_shape"]
+           "code_shape", "scale_shape", "kvq_fp16_to_kv", "kvq_kv_to_fp16", "kvq_kv_to_fp16_prefix",
+           "kvq_bytes_per_token", "compact_shape", "KVQ_FMT_FP8", "KVQ_FMT_Q4", "KVQ_FMT_Q6",
+           "KVQ_FMT_Q8", "KVQ_FMT_FP16"]
+
+# per-tensor formats (include/kvq.h)
+KVQ_FMT_FP8, KVQ_FMT_Q4, KVQ_FMT_Q6, KVQ_FMT_Q8, KVQ_FMT_FP16 = 0, 4, 6, 8, 16
 
 KVQ_OK = 0
 ERRORS = {-1: "KVQ_ERR_NULL", -2: "KVQ_ERR_WBITS", -3: "KVQ_ERR_SHAPE", -4: "KVQ_ERR_RANGE",
@@ -70,6 +75,13 @@ def load_library():
             "kvq_version": (_i, []),
             "kvq_selftest_codes": (_i, [_vp, _i64, _vp, _i64, _i, _i, _vp, _vp]),
             "kvq_selftest_scales": (_i, [_vp, _i64, _i, _vp, _vp]),
+            "kvq_fp16_to_kv": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, Shape, _i, _i, _i, _i,
+                                    _vp, _vp, _i, _vp]),
+            "kvq_kv_to_fp16": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, Shape, _i, _i, _i, _i,
+                                    _vp, _vp, _i, _vp]),
+            "kvq_kv_to_fp16_prefix": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, Shape, _i, _i, _i,
+                                           _vp, _vp, _i, _vp]),
+            "kvq_bytes_per_token": (_i64, [_i, _i, _i]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -236,6 +248,106 @@ def kvq_q_to_fp16_kv(k_in, k_out, k_scales, v_in, v_out, v_scales, batch_size, o
     codes, k_out/v_out the fp16 caches)."""
     _q_common(False, k_in, k_out, k_scales, v_in, v_out, v_scales, batch_size, offset, width,
               page_size, cache_seqlens, block_table, wbits, stream)
+
+
+# ---------------------------------------------------------------- per-tensor formats
+def compact_shape(cache_shape, fmt):
+    """Shape of a tensor's compact form: uint8 of the cache shape for the
+    8-bit format, the code shape for the block formats."""
+    return tuple(cache_shape) if fmt == KVQ_FMT_FP8 else code_shape(cache_shape, fmt)
+
+
+def _kv_ptrs(to_compact, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v):
+    torch = _torch()
+    ref = None
+    for t in ((k_in, v_in) if to_compact else (k_out, v_out)):
+        if t is not None:
+            ref = t
+            break
+    if ref is None:
+        raise ValueError("at least one of K and V is required")
+    shp = _shape4(ref, "cache")
+    dev = ref.device
+    ptrs = []
+    for name, (src, dst, sc, fmt) in (("k", (k_in, k_out, k_scales, fmt_k)), ("v", (v_in, v_out, v_scales, fmt_v))):
+        if src is None and dst is None:
+            ptrs += [None, None, _dev_ptr(sc, name + "_scales", torch.float16, dev) if sc is not None else None]
+            continue
+        if fmt not in (0, 4, 6, 8):
+            raise ValueError("%s format must be KVQ_FMT_FP8, Q4, Q6 or Q8" % name)
+        cshape = compact_shape(shp, fmt)
+        f16, comp = (src, dst) if to_compact else (dst, src)
+        pf16 = _dev_ptr(f16, name + " fp16 cache", torch.float16, dev)
+        pcomp = _dev_ptr(comp, name + " compact cache", torch.uint8, dev)
+        _expect_shape(f16, shp, name + " fp16 cache")
+        _expect_shape(comp, cshape, name + " compact cache")
+        psc = None
+        if sc is not None:
+            psc = _dev_ptr(sc, name + "_scales", torch.float16, dev)
+            _expect_shape(sc, scale_shape(shp), name + "_scales")
+        ptrs += ([pf16, pcomp, psc] if to_compact else [pcomp, pf16, psc])
+    return ptrs, shp, dev
+
+
+def _tables(batch_size, cache_seqlens, block_table, dev):
+    if block_table.dim() != 2 or block_table.shape[0] < batch_size:
+        raise ValueError("block_table must be [>= batch_size, cols]")
+    if cache_seqlens.dim() != 1 or cache_seqlens.shape[0] < batch_size:
+        raise ValueError("cache_seqlens must be [>= batch_size]")
+    return (_table_ptr(cache_seqlens, "cache_seqlens", dev), _table_ptr(block_table, "block_table", dev),
+            int(block_table.shape[1]))
+
+
+def _per_tensor(fname, to_compact, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v,
+                batch_size, offset, width, page_size, cache_seqlens, block_table, stream):
+    ptrs, shp, dev = _kv_ptrs(to_compact, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v)
+    psl = pbt = None
+    cols = 0
+    if page_size:
+        if cache_seqlens is None or block_table is None:
+            raise ValueError("paged mode needs cache_seqlens and block_table")
+        psl, pbt, cols = _tables(batch_size, cache_seqlens, block_table, dev)
+    rc = getattr(load_library(), fname)(ptrs[0], ptrs[1], ptrs[2], int(fmt_k), ptrs[3], ptrs[4], ptrs[5],
+                                        int(fmt_v), Shape(*shp), int(batch_size), int(offset), int(width),
+                                        int(page_size), psl, pbt, cols, _stream_handle(stream, dev))
+    _check(rc, fname)
+
+
+def kvq_fp16_to_kv(k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v, batch_size, offset,
+                   width, page_size=0, cache_seqlens=None, block_table=None, stream=None):
+    """fp16 K/V -> per-tensor formats in one launch (KVQ_FMT_FP8: uint8 cache,
+    no scales; KVQ_FMT_Q4/Q6/Q8: codes + fp16 scales).  Pass None for the
+    three tensors of an absent half."""
+    _per_tensor("kvq_fp16_to_kv", True, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v,
+                batch_size, offset, width, page_size, cache_seqlens, block_table, stream)
+
+
+def kvq_kv_to_fp16(k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v, batch_size, offset,
+                   width, page_size=0, cache_seqlens=None, block_table=None, stream=None):
+    """Per-tensor formats -> fp16 K/V in one launch over the same rows."""
+    _per_tensor("kvq_kv_to_fp16", False, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v,
+                batch_size, offset, width, page_size, cache_seqlens, block_table, stream)
+
+
+def kvq_kv_to_fp16_prefix(k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v, batch_size,
+                          width, max_len, cache_seqlens, block_table, stream=None):
+    """Widen positions [0, min(cache_seqlens[b] + width, max_len)) of every
+    sequence of a paged cache (page_size = the caches' dim 1)."""
+    ptrs, shp, dev = _kv_ptrs(False, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v)
+    psl, pbt, cols = _tables(batch_size, cache_seqlens, block_table, dev)
+    rc = load_library().kvq_kv_to_fp16_prefix(ptrs[0], ptrs[1], ptrs[2], int(fmt_k), ptrs[3], ptrs[4],
+                                              ptrs[5], int(fmt_v), Shape(*shp), int(batch_size),
+                                              int(width), int(max_len), psl, pbt, cols,
+                                              _stream_handle(stream, dev))
+    _check(rc, "kvq_kv_to_fp16_prefix")
+
+
+def kvq_bytes_per_token(fmt, heads, head_dim):
+    """Bytes one token occupies in one cache tensor of a format (host only)."""
+    rc = load_library().kvq_bytes_per_token(int(fmt), int(heads), int(head_dim))
+    if rc < 0:
+        raise KvqError(int(rc), "kvq_bytes_per_token")
+    return int(rc)
 
 
 # ---------------------------------------------------------------- host prefix compare

@@ -86,17 +86,45 @@ int fp8_call(bool to_fp8, const void* in, void* out, kvq_shape s, int batch_size
     return err ? KVQ_ERR_HIP : KVQ_OK;
 }
 
-int q_call(bool quant, const void* k_src, void* k_dst, const void* k_scales, const void* v_src,
-           void* v_dst, const void* v_scales, kvq_shape s, int batch_size, int offset, int width,
-           int page_size, const int32_t* cache_seqlens, const int32_t* block_table,
-           int block_table_cols, int wbits, void* stream) {
-    if (wbits != 4 && wbits != 6 && wbits != 8) return KVQ_ERR_WBITS;
-    const bool k_any = k_src || k_dst || k_scales, k_all = k_src && k_dst && k_scales;
-    const bool v_any = v_src || v_dst || v_scales, v_all = v_src && v_dst && v_scales;
-    if ((k_any && !k_all) || (v_any && !v_all) || (!k_any && !v_any)) return KVQ_ERR_NULL;
+bool valid_fmt(int f) { return f == 0 || f == 4 || f == 6 || f == 8; }
+
+// bytes of one row's compact form and of its scales, for format f
+int64_t compact_row_bytes(int64_t R, int f) { return f == 0 ? R : R / 8 * f; }
+int64_t scale_row_bytes(int64_t R, int f) { return f == 0 ? 0 : (R / 32) * 2; }
+
+enum CallKind { kSingleWidth, kPerTensor, kPrefixWiden };
+
+// Shared validation and dispatch of every K/V conversion.  to_compact: fp16
+// sources, compact destinations; otherwise the reverse.  For kSingleWidth
+// fmt_k == fmt_v == wbits; for kPrefixWiden offset is unused and max_len
+// bounds the positions per sequence.
+int kv_call(CallKind kind, bool to_compact, const void* k_src, void* k_dst, const void* k_scales, int fmt_k,
+            const void* v_src, void* v_dst, const void* v_scales, int fmt_v, kvq_shape s, int batch_size,
+            int offset, int width, int page_size, int max_len, const int32_t* cache_seqlens,
+            const int32_t* block_table, int block_table_cols, void* stream) {
+    const bool k_present = k_src || k_dst, v_present = v_src || v_dst;
+    if (kind == kSingleWidth) {
+        const bool k_any = k_present || k_scales, v_any = v_present || v_scales;
+        if ((k_any && !(k_src && k_dst && k_scales)) || (v_any && !(v_src && v_dst && v_scales)) ||
+            (!k_any && !v_any))
+            return KVQ_ERR_NULL;
+    } else {
+        if ((k_present && !(k_src && k_dst)) || (v_present && !(v_src && v_dst)) || (!k_present && !v_present))
+            return KVQ_ERR_NULL;
+        if ((k_present && !valid_fmt(fmt_k)) || (v_present && !valid_fmt(fmt_v))) return KVQ_ERR_WBITS;
+        if (k_present && ((fmt_k == 0) != (k_scales == nullptr))) return KVQ_ERR_NULL;
+        if (v_present && ((fmt_v == 0) != (v_scales == nullptr))) return KVQ_ERR_NULL;
+        if (!k_present && k_scales) return KVQ_ERR_NULL;
+        if (!v_present && v_scales) return KVQ_ERR_NULL;
+    }
     int rc = check_shape(s, true);
     if (rc) return rc;
-    if (page_size < 0) return KVQ_ERR_RANGE;
+    if (kind == kPrefixWiden) {
+        page_size = s.dim1;
+        if (batch_size < 0 || width < 0 || max_len < 0 || block_table_cols <= 0) return KVQ_ERR_RANGE;
+    } else if (page_size < 0) {
+        return KVQ_ERR_RANGE;
+    }
     if (page_size == 0) {
         rc = check_contig_window(s, batch_size, offset, width);
         if (rc) return rc;
@@ -110,34 +138,54 @@ int q_call(bool quant, const void* k_src, void* k_dst, const void* k_scales, con
     const int64_t R = (int64_t)s.heads * s.head_dim;
     // work units (row segments of K and V) are numbered in 32 bits
     const int64_t max_seg = (R / 8 + 63) / 64;
-    if ((int64_t)batch_size * width * 2 * max_seg > INT32_MAX / 2) return KVQ_ERR_RANGE;
+    const int64_t per_seq = kind == kPrefixWiden ? max_len : width;
+    if ((int64_t)batch_size * per_seq * 2 * max_seg > INT32_MAX / 2) return KVQ_ERR_RANGE;
     const void* ptrs[6] = {k_src, k_dst, k_scales, v_src, v_dst, v_scales};
     for (const void* p : ptrs)
         if (p && !aligned(p, 16)) return KVQ_ERR_ALIGN;
 
     const int64_t rows = (int64_t)s.dim0 * s.dim1;
-    const int64_t f16_bytes = rows * R * 2, code_bytes = rows * R / 8 * wbits, scale_bytes = rows * (R / 32) * 2;
-    const int64_t src_bytes = quant ? f16_bytes : code_bytes, dst_bytes = quant ? code_bytes : f16_bytes;
+    auto f16b = [&](void) { return rows * R * 2; };
+    const int64_t k_compact = rows * compact_row_bytes(R, fmt_k), v_compact = rows * compact_row_bytes(R, fmt_v);
     const Extent ext[8] = {
-        {k_src, src_bytes, false}, {k_dst, dst_bytes, true}, {k_scales, scale_bytes, quant},
-        {v_src, src_bytes, false}, {v_dst, dst_bytes, true}, {v_scales, scale_bytes, quant},
+        {k_src, to_compact ? f16b() : k_compact, false}, {k_dst, to_compact ? k_compact : f16b(), true},
+        {k_scales, rows * scale_row_bytes(R, fmt_k), to_compact},
+        {v_src, to_compact ? f16b() : v_compact, false}, {v_dst, to_compact ? v_compact : f16b(), true},
+        {v_scales, rows * scale_row_bytes(R, fmt_v), to_compact},
         {cache_seqlens, page_size ? (int64_t)batch_size * 4 : 0, false},
         {block_table, page_size ? (int64_t)batch_size * block_table_cols * 4 : 0, false}};
     if (any_output_overlap(ext, 8)) return KVQ_ERR_OVERLAP;
-    if (batch_size == 0 || width == 0) return KVQ_OK;
+    if (batch_size == 0 || per_seq == 0) return KVQ_OK;
 
     QLaunch a;
-    a.k_src = k_src; a.k_dst = k_dst; a.k_scales = const_cast<void*>(k_scales);
-    a.v_src = v_src; a.v_dst = v_dst; a.v_scales = const_cast<void*>(v_scales);
+    a.k_src = k_present ? k_src : nullptr; a.k_dst = k_present ? k_dst : nullptr;
+    a.k_scales = const_cast<void*>(k_scales);
+    a.v_src = v_present ? v_src : nullptr; a.v_dst = v_present ? v_dst : nullptr;
+    a.v_scales = const_cast<void*>(v_scales);
     a.dim0 = s.dim0; a.dim1 = s.dim1; a.R = (int32_t)R;
-    a.batch = batch_size; a.offset = offset; a.width = width;
+    a.batch = batch_size; a.offset = kind == kPrefixWiden ? 0 : offset; a.width = width;
     a.page_size = page_size;
     a.cache_seqlens = page_size ? cache_seqlens : nullptr;
     a.block_table = page_size ? block_table : nullptr;
     a.bt_cols = page_size ? block_table_cols : 0;
-    a.wbits = wbits;
-    const int err = quant ? kvq::launch_quant_kv(a, stream) : kvq::launch_dequant_kv(a, stream);
+    a.wbits = fmt_k;
+    a.fmt_k = fmt_k; a.fmt_v = fmt_v;
+    a.max_len = max_len;
+    int err;
+    if (kind == kSingleWidth) err = to_compact ? kvq::launch_quant_kv(a, stream) : kvq::launch_dequant_kv(a, stream);
+    else if (kind == kPerTensor) err = to_compact ? kvq::launch_fp16_to_kv(a, stream) : kvq::launch_kv_to_fp16(a, stream);
+    else err = kvq::launch_kv_to_fp16_prefix(a, stream);
     return err ? KVQ_ERR_HIP : KVQ_OK;
+}
+
+int q_call(bool quant, const void* k_src, void* k_dst, const void* k_scales, const void* v_src,
+           void* v_dst, const void* v_scales, kvq_shape s, int batch_size, int offset, int width,
+           int page_size, const int32_t* cache_seqlens, const int32_t* block_table,
+           int block_table_cols, int wbits, void* stream) {
+    if (wbits != 4 && wbits != 6 && wbits != 8) return KVQ_ERR_WBITS;
+    return kv_call(kSingleWidth, quant, k_src, k_dst, k_scales, wbits, v_src, v_dst, v_scales, wbits, s,
+                   batch_size, offset, width, page_size, 0, cache_seqlens, block_table, block_table_cols,
+                   stream);
 }
 
 }  // namespace
@@ -169,6 +217,42 @@ int kvq_q_to_fp16_kv(const void* k_in, void* k_out, const void* k_scales, const 
                      void* hip_stream) {
     return q_call(false, k_in, k_out, k_scales, v_in, v_out, v_scales, s, batch_size, offset, width,
                   page_size, cache_seqlens, block_table, block_table_cols, wbits, hip_stream);
+}
+
+int kvq_fp16_to_kv(const void* k_in, void* k_out, void* k_scales, int fmt_k, const void* v_in,
+                   void* v_out, void* v_scales, int fmt_v, kvq_shape s, int batch_size, int offset,
+                   int width, int page_size, const int32_t* cache_seqlens, const int32_t* block_table,
+                   int block_table_cols, void* hip_stream) {
+    return kv_call(kPerTensor, true, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v, s,
+                   batch_size, offset, width, page_size, 0, cache_seqlens, block_table, block_table_cols,
+                   hip_stream);
+}
+
+int kvq_kv_to_fp16(const void* k_in, void* k_out, const void* k_scales, int fmt_k, const void* v_in,
+                   void* v_out, const void* v_scales, int fmt_v, kvq_shape s, int batch_size, int offset,
+                   int width, int page_size, const int32_t* cache_seqlens, const int32_t* block_table,
+                   int block_table_cols, void* hip_stream) {
+    return kv_call(kPerTensor, false, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v, s,
+                   batch_size, offset, width, page_size, 0, cache_seqlens, block_table, block_table_cols,
+                   hip_stream);
+}
+
+int kvq_kv_to_fp16_prefix(const void* k_in, void* k_out, const void* k_scales, int fmt_k,
+                          const void* v_in, void* v_out, const void* v_scales, int fmt_v, kvq_shape s,
+                          int batch_size, int width, int max_len, const int32_t* cache_seqlens,
+                          const int32_t* block_table, int block_table_cols, void* hip_stream) {
+    return kv_call(kPrefixWiden, false, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v, s,
+                   batch_size, 0, width, s.dim1, max_len, cache_seqlens, block_table, block_table_cols,
+                   hip_stream);
+}
+
+int64_t kvq_bytes_per_token(int format, int heads, int head_dim) {
+    if (format != 16 && !valid_fmt(format)) return KVQ_ERR_WBITS;
+    if (heads <= 0 || head_dim <= 0) return KVQ_ERR_SHAPE;
+    if (format != 16 && format != 0 && head_dim % 32 != 0) return KVQ_ERR_SHAPE;
+    const int64_t R = (int64_t)heads * head_dim;
+    if (format == 16) return 2 * R;
+    return compact_row_bytes(R, format) + scale_row_bytes(R, format);
 }
 
 // Matching prefix in 64-bit chunks (ExLlamaV2 cache page, Description of

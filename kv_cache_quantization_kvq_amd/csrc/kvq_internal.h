@@ -32,7 +32,9 @@ struct QLaunch {
     const int32_t* cache_seqlens; // paged only
     const int32_t* block_table;   // paged only, [batch, bt_cols]
     int32_t bt_cols;
-    int32_t wbits;
+    int32_t wbits;                // single-width calls
+    int32_t fmt_k, fmt_v;         // per-tensor calls: 0 = 8-bit high byte, 4/6/8 = block codes
+    int32_t max_len;              // full-prefix calls: positions enumerated per sequence
 };
 
 // Launchers (return a hipError_t value as int, 0 on success).
@@ -40,6 +42,9 @@ int launch_fp16_to_fp8(const Fp8Launch& a, void* stream);
 int launch_fp8_to_fp16(const Fp8Launch& a, void* stream);
 int launch_quant_kv(const QLaunch& a, void* stream);
 int launch_dequant_kv(const QLaunch& a, void* stream);
+int launch_fp16_to_kv(const QLaunch& a, void* stream);
+int launch_kv_to_fp16(const QLaunch& a, void* stream);
+int launch_kv_to_fp16_prefix(const QLaunch& a, void* stream);
 
 // Element-level self-test launchers (same device routines as the kernels).
 int launch_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s, int64_t ns,

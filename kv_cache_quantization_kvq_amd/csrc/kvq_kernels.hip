@@ -53,18 +53,32 @@ __device__ __forceinline__ void st_nt(uint4* p, uint4 v) {
 
 // ---------------------------------------------------------------- row map
 
-// Physical row of logical row n = b * width + t, or -1 when skipped.
-// Contiguous: (b, offset + t).  Paged: position p = cache_seqlens[b] +
-// offset + t in page block_table[b][p / page_size], slot p % page_size;
-// skipped if p < 0, past the table, or the page is outside [0, dim0).
-// All values are wave-uniform (scalar loads and SALU).
-template <bool PAGED>
+// How logical rows map to cache rows.
+enum RowMode {
+    kContig = 0,   // n = b * width + t -> row (b, offset + t)
+    kPaged = 1,    // n = b * width + t -> position cache_seqlens[b] + offset + t
+    kPrefix = 2,   // n = b * max_len + p -> position p, live while p < cache_seqlens[b] + width
+};
+
+// Physical row of logical row n, or -1 when skipped.  Paged positions p live
+// in page block_table[b][p / page_size], slot p % page_size, and are skipped
+// if p < 0, past the table, or the page is outside [0, dim0).  All values
+// are wave-uniform (scalar loads and SALU).
+template <int MODE>
 __device__ __forceinline__ int64_t resolve_row(const QLaunch& a, int32_t n) {
-    const int32_t b = n / a.width;
-    const int32_t t = n - b * a.width;
-    if (!PAGED) return (int64_t)b * a.dim1 + a.offset + t;
-    const int64_t p = (int64_t)a.cache_seqlens[b] + a.offset + t;
-    if (p < 0 || p >= (int64_t)a.bt_cols * a.page_size) return -1;
+    const int32_t per_seq = MODE == kPrefix ? a.max_len : a.width;
+    const int32_t b = n / per_seq;
+    const int32_t t = n - b * per_seq;
+    if (MODE == kContig) return (int64_t)b * a.dim1 + a.offset + t;
+    int64_t p;
+    if (MODE == kPrefix) {
+        p = t;
+        if (p >= (int64_t)a.cache_seqlens[b] + a.width) return -1;
+    } else {
+        p = (int64_t)a.cache_seqlens[b] + a.offset + t;
+        if (p < 0) return -1;
+    }
+    if (p >= (int64_t)a.bt_cols * a.page_size) return -1;
     const uint32_t pu = (uint32_t)p;
     const uint32_t pi = pu / (uint32_t)a.page_size;
     const int32_t page = a.block_table[(int64_t)b * a.bt_cols + pi];
@@ -80,7 +94,7 @@ __device__ __forceinline__ int64_t resolve_row(const QLaunch& a, int32_t n) {
 // touch neighbouring memory.  One wavefront converts one unit.
 
 struct QGeom {
-    int32_t n_units;   // batch * width * ntens * nseg
+    int32_t n_units;   // rows * ntens * nseg
     int32_t nseg;      // row segments per row
     int32_t ntens;     // tensors present: 1 or 2
     int32_t tens0;     // the tensor when ntens == 1: 0 = K, 1 = V
@@ -96,7 +110,7 @@ struct UnitRef {
 // Dead units (grid padding past n_units, skipped rows) still read row 0 of
 // their tensor (always in bounds) and only have their stores masked off, so
 // no branch splits a wave's load stream.
-template <bool PAGED>
+template <int MODE>
 __device__ __forceinline__ UnitRef unit_ref(const QLaunch& a, const QGeom& g, int32_t u) {
     UnitRef r;
     r.live = u < g.n_units;
@@ -115,36 +129,45 @@ __device__ __forceinline__ UnitRef unit_ref(const QLaunch& a, const QGeom& g, in
         n = rt;
         r.tensor = g.tens0;
     }
-    const int64_t row = resolve_row<PAGED>(a, n);
+    const int64_t row = resolve_row<MODE>(a, n);
     r.live = r.live && row >= 0;
     r.row = row >= 0 ? row : 0;
     return r;
 }
 
-// ---------------------------------------------------------------- quantize
+__device__ __forceinline__ int32_t wave_index() {
+    return (int32_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// ---------------------------------------------------------------- fp16 -> compact
 //
 // Lane l of segment g owns the 16 consecutive elements of piece
 // pc = 64 g + l (two 128-bit loads); a 32-element block is one lane pair, so
 // the block absmax is one DPP exchange.  A segment is 1024 elements; GUARD
 // masks the pieces past the row end of a partial last segment (pieces per
 // row are even, so a lane pair is in or out together).
-template <int WBITS, bool PAGED, bool GUARD>
-__global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, QGeom g) {
-    const int lane = threadIdx.x & 63;
-    const int32_t wave = (int32_t)blockIdx.x * kWaves +
-                         __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const UnitRef ur = unit_ref<PAGED>(a, g, wave);
-    const int32_t R = a.R;
-    const int32_t pc = ur.seg * 64 + lane;
-    const bool in = !GUARD || pc < (R >> 4);
 
+template <bool GUARD>
+__device__ __forceinline__ void load_piece(const QLaunch& a, const UnitRef& ur, int32_t pc, bool in,
+                                           uint4& x0, uint4& x1) {
     const uint4* src = reinterpret_cast<const uint4*>(
-        static_cast<const uint16_t*>(ur.tensor ? a.v_src : a.k_src) + ur.row * R) + 2 * pc;
-    uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
+        static_cast<const uint16_t*>(ur.tensor ? a.v_src : a.k_src) + ur.row * a.R) + 2 * pc;
+    x0 = make_uint4(0, 0, 0, 0);
+    x1 = make_uint4(0, 0, 0, 0);
     if (in) {
         x0 = ld_nt(src);
         x1 = ld_nt(src + 1);
     }
+}
+
+// Block quantization of one unit.
+template <int WBITS, bool GUARD>
+__device__ __forceinline__ void quant_unit(const QLaunch& a, const UnitRef& ur, int lane) {
+    const int32_t R = a.R;
+    const int32_t pc = ur.seg * 64 + lane;
+    const bool in = !GUARD || pc < (R >> 4);
+    uint4 x0, x1;
+    load_piece<GUARD>(a, ur, pc, in, x0, x1);
     const uint32_t s16 = scale_from_absmax<WBITS>(pair_max(absmax_2chunks(x0, x1)));
     const ScaleOps so = prep_scale(s16);
     uint32_t u0[8], u1[8];
@@ -174,13 +197,50 @@ __global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, QGeom g) 
     if (store && (lane & 1) == 0) scales[pc >> 1] = (uint16_t)s16;
 }
 
-// ---------------------------------------------------------------- dequantize
+// high byte of each fp16: bytes 1,3 of the first word then 1,3 of the second
+__device__ __forceinline__ uint32_t high_bytes(uint32_t w0, uint32_t w1) {
+    return __builtin_amdgcn_perm(w1, w0, 0x07050301u);
+}
+
+// 8-bit (high byte) narrowing of one unit: 16 bytes per lane.
+template <bool GUARD>
+__device__ __forceinline__ void narrow_unit(const QLaunch& a, const UnitRef& ur, int lane) {
+    const int32_t pc = ur.seg * 64 + lane;
+    const bool in = !GUARD || pc < (a.R >> 4);
+    uint4 x0, x1;
+    load_piece<GUARD>(a, ur, pc, in, x0, x1);
+    const uint4 d = make_uint4(high_bytes(x0.x, x0.y), high_bytes(x0.z, x0.w),
+                               high_bytes(x1.x, x1.y), high_bytes(x1.z, x1.w));
+    uint8_t* out = static_cast<uint8_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * (int64_t)a.R;
+    if (ur.live && in) *reinterpret_cast<uint4*>(out + 16 * pc) = d;
+}
+
+template <int WBITS, int MODE, bool GUARD>
+__global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, QGeom g) {
+    const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
+    quant_unit<WBITS, GUARD>(a, ur, threadIdx.x & 63);
+}
+
+// Per-tensor formats: the unit's tensor picks its format (wave-uniform).
+template <int MODE, bool GUARD>
+__global__ __launch_bounds__(kThreads) void narrow_kv_kernel(QLaunch a, QGeom g) {
+    const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
+    const int lane = threadIdx.x & 63;
+    switch (ur.tensor ? a.fmt_v : a.fmt_k) {
+        case 4: quant_unit<4, GUARD>(a, ur, lane); break;
+        case 6: quant_unit<6, GUARD>(a, ur, lane); break;
+        case 8: quant_unit<8, GUARD>(a, ur, lane); break;
+        default: narrow_unit<GUARD>(a, ur, lane); break;
+    }
+}
+
+// ---------------------------------------------------------------- compact -> fp16
 //
 // Lane l holds chunks (8 elements) c = NCH * 64 g + 64 k + l, k < NCH, so
 // every 128-bit store of the wave is contiguous.
 
 struct CodeChunk {
-    uint32_t lo, hi;    // Q4: lo = 8 codes; Q6: the 8 bytes holding the 6 code bytes
+    uint32_t lo, hi;    // Q4: lo = 8 codes; Q6: the 8 bytes holding the 6 code bytes; Q8: 8 codes
     uint32_t s;         // scale (fp16 bits)
 };
 
@@ -228,12 +288,9 @@ __device__ __forceinline__ uint4 dequant_chunk(const CodeChunk& q, int32_t c) {
     }
 }
 
-template <int WBITS, bool PAGED, int NCH, bool GUARD>
-__global__ __launch_bounds__(kThreads) void dequant_kv_kernel(QLaunch a, QGeom g) {
-    const int lane = threadIdx.x & 63;
-    const int32_t wave = (int32_t)blockIdx.x * kWaves +
-                         __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const UnitRef ur = unit_ref<PAGED>(a, g, wave);
+// Block dequantization of one unit.
+template <int WBITS, int NCH, bool GUARD>
+__device__ __forceinline__ void dequant_unit(const QLaunch& a, const UnitRef& ur, int lane) {
     const int32_t R = a.R;
     const int32_t cpr = R >> 3;
     const uint8_t* codes = static_cast<const uint8_t*>(ur.tensor ? a.v_src : a.k_src) +
@@ -252,23 +309,59 @@ __global__ __launch_bounds__(kThreads) void dequant_kv_kernel(QLaunch a, QGeom g
     for (int k = 0; k < NCH; ++k) {
         const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
         const uint4 o = dequant_chunk<WBITS>(q[k], c);
-        if (ur.live && (!GUARD || c < cpr)) {
-            st_nt(dst + c, o);
-        }
+        if (ur.live && (!GUARD || c < cpr)) st_nt(dst + c, o);
     }
-}
-
-// ---------------------------------------------------------------- 8-bit
-
-// high byte of each fp16: bytes 1,3 of the first word then 1,3 of the second
-__device__ __forceinline__ uint32_t high_bytes(uint32_t w0, uint32_t w1) {
-    return __builtin_amdgcn_perm(w1, w0, 0x07050301u);
 }
 
 // bytes 0,1 of w -> fp16 patterns byte << 8 in the low and high halves
 __device__ __forceinline__ uint32_t widen_lo(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x01040004u); }
 __device__ __forceinline__ uint32_t widen_hi(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x03040204u); }
 
+// 8-bit (high byte) widening of one unit.
+template <int NCH, bool GUARD>
+__device__ __forceinline__ void widen_unit(const QLaunch& a, const UnitRef& ur, int lane) {
+    const int32_t R = a.R;
+    const int32_t cpr = R >> 3;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(
+        static_cast<const uint8_t*>(ur.tensor ? a.v_src : a.k_src) + ur.row * (int64_t)R);
+    uint2 v[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
+        v[k] = make_uint2(0, 0);
+        if (!GUARD || c < cpr) v[k] = make_uint2(ld_nt(src + 2 * c), ld_nt(src + 2 * c + 1));
+    }
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * R);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
+        const uint4 o = make_uint4(widen_lo(v[k].x), widen_hi(v[k].x), widen_lo(v[k].y), widen_hi(v[k].y));
+        if (ur.live && (!GUARD || c < cpr)) st_nt(dst + c, o);
+    }
+}
+
+template <int WBITS, int MODE, int NCH, bool GUARD>
+__global__ __launch_bounds__(kThreads) void dequant_kv_kernel(QLaunch a, QGeom g) {
+    const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
+    dequant_unit<WBITS, NCH, GUARD>(a, ur, threadIdx.x & 63);
+}
+
+template <int MODE, int NCH, bool GUARD>
+__global__ __launch_bounds__(kThreads) void widen_kv_kernel(QLaunch a, QGeom g) {
+    const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
+    const int lane = threadIdx.x & 63;
+    switch (ur.tensor ? a.fmt_v : a.fmt_k) {
+        case 4: dequant_unit<4, NCH, GUARD>(a, ur, lane); break;
+        case 6: dequant_unit<6, NCH, GUARD>(a, ur, lane); break;
+        case 8: dequant_unit<8, NCH, GUARD>(a, ur, lane); break;
+        default: widen_unit<NCH, GUARD>(a, ur, lane); break;
+    }
+}
+
+// ---------------------------------------------------------------- 8-bit
+
+// Contiguous windows: each sequence's window is one run of width * R
+// elements, streamed 8 elements per chunk, kFp8Cpt chunks per thread.
 __global__ __launch_bounds__(kThreads) void fp16_to_fp8_kernel(Fp8Launch a) {
     const int64_t cps = a.span_elems >> 3;
     const int64_t c0 = (int64_t)blockIdx.x * (kThreads * kFp8Cpt) + threadIdx.x;
@@ -372,34 +465,56 @@ int launch_fp8_to_fp16(const Fp8Launch& a, void* stream) {
     return launch(reinterpret_cast<const void*>(&fp8_to_fp16_kernel), fp8_grid(a), dim3(kThreads), args, stream);
 }
 
-// Kernel variant for a call.  Quantize: 64 lanes x 16 elements per
-// segment, guarded when the row's 16-element pieces are not a multiple of
-// 64.  Dequantize: NCH chunks of 8 per lane, NCH = 2 (or 1) when the row's
-// chunks are a multiple of 128 (or 64), else NCH = 2 guarded.
-template <int WBITS, bool PAGED>
+// Kernel variants.  fp16 -> compact: 64 lanes x 16 elements per segment,
+// guarded when the row's 16-element pieces are not a multiple of 64.
+// compact -> fp16: NCH chunks of 8 per lane, NCH = 2 (or 1) when the row's
+// chunks are a multiple of 128 (or 64), else NCH = 2 guarded.  The
+// single-format kernels serve the page's one-wbits calls; the per-tensor
+// kernels pick each unit's format at run time.
+template <int W, int MODE>
 static const void* quant_fn(bool guard) {
-    return guard ? reinterpret_cast<const void*>(&quant_kv_kernel<WBITS, PAGED, true>)
-                 : reinterpret_cast<const void*>(&quant_kv_kernel<WBITS, PAGED, false>);
+    return guard ? reinterpret_cast<const void*>(&quant_kv_kernel<W, MODE, true>)
+                 : reinterpret_cast<const void*>(&quant_kv_kernel<W, MODE, false>);
 }
 
-template <int WBITS, bool PAGED>
+template <int MODE>
+static const void* narrow_fn(bool guard) {
+    return guard ? reinterpret_cast<const void*>(&narrow_kv_kernel<MODE, true>)
+                 : reinterpret_cast<const void*>(&narrow_kv_kernel<MODE, false>);
+}
+
+template <int W, int MODE>
 static const void* dequant_fn(int nch, bool guard) {
-    if (guard) return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, PAGED, 2, true>);
-    if (nch == 2) return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, PAGED, 2, false>);
-    return reinterpret_cast<const void*>(&dequant_kv_kernel<WBITS, PAGED, 1, false>);
+    if (guard) return reinterpret_cast<const void*>(&dequant_kv_kernel<W, MODE, 2, true>);
+    if (nch == 2) return reinterpret_cast<const void*>(&dequant_kv_kernel<W, MODE, 2, false>);
+    return reinterpret_cast<const void*>(&dequant_kv_kernel<W, MODE, 1, false>);
 }
 
-template <int WBITS>
-static const void* q_fn(bool quant, bool paged, int nch, bool guard) {
-    if (quant) return paged ? quant_fn<WBITS, true>(guard) : quant_fn<WBITS, false>(guard);
-    return paged ? dequant_fn<WBITS, true>(nch, guard) : dequant_fn<WBITS, false>(nch, guard);
+template <int MODE>
+static const void* widen_fn(int nch, bool guard) {
+    if (guard) return reinterpret_cast<const void*>(&widen_kv_kernel<MODE, 2, true>);
+    if (nch == 2) return reinterpret_cast<const void*>(&widen_kv_kernel<MODE, 2, false>);
+    return reinterpret_cast<const void*>(&widen_kv_kernel<MODE, 1, false>);
 }
 
-static int launch_q(const QLaunch& a, bool quant, void* stream) {
+template <int W>
+static const void* single_fn(bool to_compact, int mode, int nch, bool guard) {
+    if (to_compact) return mode == kPaged ? quant_fn<W, kPaged>(guard) : quant_fn<W, kContig>(guard);
+    return mode == kPaged ? dequant_fn<W, kPaged>(nch, guard) : dequant_fn<W, kContig>(nch, guard);
+}
+
+static const void* mixed_fn(bool to_compact, int mode, int nch, bool guard) {
+    if (to_compact) return mode == kPaged ? narrow_fn<kPaged>(guard) : narrow_fn<kContig>(guard);
+    if (mode == kPrefix) return widen_fn<kPrefix>(nch, guard);
+    return mode == kPaged ? widen_fn<kPaged>(nch, guard) : widen_fn<kContig>(nch, guard);
+}
+
+// mixed: per-tensor formats (a.fmt_k / a.fmt_v); otherwise one width a.wbits
+static int launch_units(const QLaunch& a, bool to_compact, bool mixed, int mode, void* stream) {
     int nch = 2;
     bool guard = false;
     int32_t seg_elems;
-    if (quant) {
+    if (to_compact) {
         guard = (a.R / 16) % 64 != 0;
         seg_elems = 1024;
     } else {
@@ -409,24 +524,42 @@ static int launch_q(const QLaunch& a, bool quant, void* stream) {
         else guard = true;
         seg_elems = nch * 64 * 8;
     }
+    const int64_t rows = (int64_t)a.batch * (mode == kPrefix ? a.max_len : a.width);
     QGeom g;
     g.nseg = (a.R + seg_elems - 1) / seg_elems;
     g.ntens = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
     g.tens0 = a.k_src ? 0 : 1;
-    g.n_units = (int32_t)((int64_t)a.batch * a.width * g.ntens * g.nseg);   // bounded by the host checks
+    g.n_units = (int32_t)(rows * g.ntens * g.nseg);   // bounded by the host checks
     const dim3 grid((unsigned)((g.n_units + kWaves - 1) / kWaves));
     QLaunch arg = a;
     void* args[] = {&arg, &g};
-    const bool paged = a.page_size != 0;
-    const void* fn = a.wbits == 4 ? q_fn<4>(quant, paged, nch, guard)
-                   : a.wbits == 6 ? q_fn<6>(quant, paged, nch, guard)
-                                  : q_fn<8>(quant, paged, nch, guard);
+    const void* fn;
+    if (mixed) fn = mixed_fn(to_compact, mode, nch, guard);
+    else if (a.wbits == 4) fn = single_fn<4>(to_compact, mode, nch, guard);
+    else if (a.wbits == 6) fn = single_fn<6>(to_compact, mode, nch, guard);
+    else fn = single_fn<8>(to_compact, mode, nch, guard);
     return launch(fn, grid, dim3(kThreads), args, stream);
 }
 
-int launch_quant_kv(const QLaunch& a, void* stream) { return launch_q(a, true, stream); }
+int launch_quant_kv(const QLaunch& a, void* stream) {
+    return launch_units(a, true, false, a.page_size ? kPaged : kContig, stream);
+}
 
-int launch_dequant_kv(const QLaunch& a, void* stream) { return launch_q(a, false, stream); }
+int launch_dequant_kv(const QLaunch& a, void* stream) {
+    return launch_units(a, false, false, a.page_size ? kPaged : kContig, stream);
+}
+
+int launch_fp16_to_kv(const QLaunch& a, void* stream) {
+    return launch_units(a, true, true, a.page_size ? kPaged : kContig, stream);
+}
+
+int launch_kv_to_fp16(const QLaunch& a, void* stream) {
+    return launch_units(a, false, true, a.page_size ? kPaged : kContig, stream);
+}
+
+int launch_kv_to_fp16_prefix(const QLaunch& a, void* stream) {
+    return launch_units(a, false, true, kPrefix, stream);
+}
 
 int launch_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s, int64_t ns, int wbits,
                           bool force_clamp, uint8_t* u, void* stream) {

@@ -124,7 +124,9 @@ def q4_paged(seed=SEEDS["q4_paged"], draws=1):
     return w
 
 
-def mix_paged(seed=SEEDS["mix_paged"]):
+def mix_paged(seed=SEEDS["mix_paged"], draws=1):
+    """Large paged K-Q4 / V-Q6 workload; `draws` independent (cache_seqlens,
+    block_table) pairs (the first is the workload's own) for cold rotation."""
     rng = np.random.default_rng(seed)
     shape = (16384, 256, HEADS, HEAD_DIM)
     sl, bt = paging(rng, 64, 256, 16384, 65280)
@@ -132,6 +134,7 @@ def mix_paged(seed=SEEDS["mix_paged"]):
     w.extra["device_seed"] = seed
     ids_a, ids_b, m = token_ids(rng, 65536)
     w.extra["ids_a"], w.extra["ids_b"], w.extra["match"] = ids_a, ids_b, m
+    w.extra["tables"] = [(sl, bt)] + [paging(rng, 64, 256, 16384, 65280) for _ in range(draws - 1)]
     return w
 
 

@@ -61,6 +61,17 @@ def lib():
             "orc_fp16_to_fp8_cache": (None, [_u16p, _u8p, _int, _int, _int, _int, _int, _int, _int]),
             "orc_fp8_to_fp16_cache": (None, [_u8p, _u16p, _int, _int, _int, _int, _int, _int, _int]),
             "orc_count_match": (_i64, [ctypes.c_void_p, _i64, ctypes.c_void_p, _i64, _i64, _int]),
+            "orc_fp16_to_kv": (None, [_u16p, _u8p, _u16p, _int, _u16p, _u8p, _u16p, _int,
+                                      _int, _int, _int, _int, _int, _int, _int, _int,
+                                      _i32p, _i32p, _int]),
+            "orc_kv_to_fp16": (None, [_u8p, _u16p, _u16p, _int, _u8p, _u16p, _u16p, _int,
+                                      _int, _int, _int, _int, _int, _int, _int, _int,
+                                      _i32p, _i32p, _int]),
+            "orc_prefix_rows": (_i64, [_int, _int, _int, _int, _int, _i32p, _i32p, _int, _i64p]),
+            "orc_kv_to_fp16_prefix": (None, [_u8p, _u16p, _u16p, _int, _u8p, _u16p, _u16p, _int,
+                                             _int, _int, _int, _int, _int, _int, _int,
+                                             _i32p, _i32p, _int]),
+            "orc_bytes_per_token": (_i64, [_int, _int, _int]),
             "orc_f16_decode_array": (None, [_u16p, _i64, _f64p]),
             "orc_f16_encode_array": (None, [_f64p, _i64, _u16p]),
             "orc_scale_array": (None, [_u16p, _i64, _int, _u16p]),
@@ -244,3 +255,57 @@ def count_match(a, b, max_a):
     assert a.dtype == b.dtype and a.itemsize in (4, 8)
     return int(lib().orc_count_match(a.ctypes.data, a.size, b.ctypes.data, b.size, int(max_a),
                                      a.itemsize))
+
+
+# ---------------------------------------------------------------- per-tensor formats
+# fmt 0 = 8-bit high byte (no scales); 4, 6, 8 = block codes + fp16 scales.
+def _u16(a):
+    return None if a is None else (a.view(np.uint16) if a.dtype == np.float16 else a)
+
+
+def fp16_to_kv(k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v, batch_size, offset,
+               width, page_size=0, cache_seqlens=None, block_table=None):
+    ref = k_in if k_in is not None else v_in
+    dim0, dim1, heads, head_dim = ref.shape
+    sl, bt, cols = _meta(cache_seqlens, block_table)
+    lib().orc_fp16_to_kv(
+        _p(None if k_in is None else _as_u16(k_in), _u16p), _p(k_out, _u8p), _p(_u16(k_scales), _u16p), fmt_k,
+        _p(None if v_in is None else _as_u16(v_in), _u16p), _p(v_out, _u8p), _p(_u16(v_scales), _u16p), fmt_v,
+        dim0, dim1, heads, head_dim, batch_size, offset, width, page_size, _p(sl, _i32p), _p(bt, _i32p), cols)
+
+
+def kv_to_fp16(k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v, batch_size, offset,
+               width, page_size=0, cache_seqlens=None, block_table=None):
+    ref = k_out if k_out is not None else v_out
+    dim0, dim1, heads, head_dim = ref.shape
+    sl, bt, cols = _meta(cache_seqlens, block_table)
+    lib().orc_kv_to_fp16(
+        _p(k_in, _u8p), _p(_u16(k_out), _u16p), _p(_u16(k_scales), _u16p), fmt_k,
+        _p(v_in, _u8p), _p(_u16(v_out), _u16p), _p(_u16(v_scales), _u16p), fmt_v,
+        dim0, dim1, heads, head_dim, batch_size, offset, width, page_size, _p(sl, _i32p), _p(bt, _i32p), cols)
+
+
+def prefix_rows(dim0, page_size, batch_size, width, max_len, cache_seqlens, block_table):
+    """Physical rows of positions [0, min(cache_seqlens[b] + width, max_len))
+    of every sequence, in (b, p) order, -1 where skipped."""
+    sl, bt, cols = _meta(cache_seqlens, block_table)
+    total = int(sum(max(0, min(int(x) + width, max_len)) for x in sl))
+    rows = np.empty(max(total, 1), np.int64)
+    n = lib().orc_prefix_rows(dim0, page_size, batch_size, width, max_len, _p(sl, _i32p), _p(bt, _i32p),
+                              cols, _p(rows, _i64p))
+    return rows[:n]
+
+
+def kv_to_fp16_prefix(k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v, batch_size, width,
+                      max_len, cache_seqlens, block_table):
+    ref = k_out if k_out is not None else v_out
+    dim0, dim1, heads, head_dim = ref.shape
+    sl, bt, cols = _meta(cache_seqlens, block_table)
+    lib().orc_kv_to_fp16_prefix(
+        _p(k_in, _u8p), _p(_u16(k_out), _u16p), _p(_u16(k_scales), _u16p), fmt_k,
+        _p(v_in, _u8p), _p(_u16(v_out), _u16p), _p(_u16(v_scales), _u16p), fmt_v,
+        dim0, dim1, heads, head_dim, batch_size, width, max_len, _p(sl, _i32p), _p(bt, _i32p), cols)
+
+
+def bytes_per_token(fmt, heads, head_dim):
+    return int(lib().orc_bytes_per_token(fmt, heads, head_dim))

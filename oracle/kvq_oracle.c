@@ -404,3 +404,137 @@ void orc_scale_array(const uint16_t* a_bits, int64_t n, int wbits, uint16_t* out
 {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_scale_from_absmax(a_bits[i], wbits);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Per-tensor formats (K and V may differ) and the full-prefix dequantize.   */
+/* fmt 0 = 8-bit high byte (no scales); 4, 6, 8 = block codes + fp16 scales. */
+/* ------------------------------------------------------------------------ */
+
+static void orc_narrow_row(const uint16_t* x, int64_t R, int fmt, uint8_t* out, uint16_t* scales)
+{
+    if (fmt == 0) {
+        for (int64_t j = 0; j < R; ++j) out[j] = orc_fp8_from_f16(x[j]);
+    } else {
+        orc_quant_rows(x, 1, (int)R, fmt, out, scales);
+    }
+}
+
+static void orc_widen_row(const uint8_t* in, const uint16_t* scales, int64_t R, int fmt, uint16_t* out)
+{
+    if (fmt == 0) {
+        for (int64_t j = 0; j < R; ++j) out[j] = orc_f16_from_fp8(in[j]);
+    } else {
+        orc_dequant_rows(in, scales, 1, (int)R, fmt, out);
+    }
+}
+
+/* bytes of one row's compact form, and of its scales */
+static int64_t orc_fmt_row_bytes(int64_t R, int fmt) { return fmt == 0 ? R : R * fmt / 8; }
+static int64_t orc_fmt_scale_count(int64_t R, int fmt) { return fmt == 0 ? 0 : R / ORC_BLOCK; }
+
+void orc_fp16_to_kv(const uint16_t* k_in, uint8_t* k_out, uint16_t* k_scales, int fmt_k,
+                    const uint16_t* v_in, uint8_t* v_out, uint16_t* v_scales, int fmt_v,
+                    int dim0, int dim1, int heads, int head_dim,
+                    int batch_size, int offset, int width, int page_size,
+                    const int32_t* cache_seqlens, const int32_t* block_table, int bt_cols)
+{
+    const int64_t R = (int64_t)heads * head_dim;
+    for (int b = 0; b < batch_size; ++b)
+        for (int t = 0; t < width; ++t) {
+            int64_t row = orc_resolve_row(b, t, dim0, dim1, offset, page_size,
+                                          cache_seqlens, block_table, bt_cols);
+            if (row < 0) continue;
+            if (k_in)
+                orc_narrow_row(k_in + row * R, R, fmt_k, k_out + row * orc_fmt_row_bytes(R, fmt_k),
+                               k_scales ? k_scales + row * orc_fmt_scale_count(R, fmt_k) : 0);
+            if (v_in)
+                orc_narrow_row(v_in + row * R, R, fmt_v, v_out + row * orc_fmt_row_bytes(R, fmt_v),
+                               v_scales ? v_scales + row * orc_fmt_scale_count(R, fmt_v) : 0);
+        }
+}
+
+static void orc_widen_kv_row(int64_t row, int64_t R,
+                             const uint8_t* k_in, uint16_t* k_out, const uint16_t* k_scales, int fmt_k,
+                             const uint8_t* v_in, uint16_t* v_out, const uint16_t* v_scales, int fmt_v)
+{
+    if (k_in)
+        orc_widen_row(k_in + row * orc_fmt_row_bytes(R, fmt_k),
+                      k_scales ? k_scales + row * orc_fmt_scale_count(R, fmt_k) : 0, R, fmt_k,
+                      k_out + row * R);
+    if (v_in)
+        orc_widen_row(v_in + row * orc_fmt_row_bytes(R, fmt_v),
+                      v_scales ? v_scales + row * orc_fmt_scale_count(R, fmt_v) : 0, R, fmt_v,
+                      v_out + row * R);
+}
+
+void orc_kv_to_fp16(const uint8_t* k_in, uint16_t* k_out, const uint16_t* k_scales, int fmt_k,
+                    const uint8_t* v_in, uint16_t* v_out, const uint16_t* v_scales, int fmt_v,
+                    int dim0, int dim1, int heads, int head_dim,
+                    int batch_size, int offset, int width, int page_size,
+                    const int32_t* cache_seqlens, const int32_t* block_table, int bt_cols)
+{
+    const int64_t R = (int64_t)heads * head_dim;
+    for (int b = 0; b < batch_size; ++b)
+        for (int t = 0; t < width; ++t) {
+            int64_t row = orc_resolve_row(b, t, dim0, dim1, offset, page_size,
+                                          cache_seqlens, block_table, bt_cols);
+            if (row < 0) continue;
+            orc_widen_kv_row(row, R, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v);
+        }
+}
+
+/* Paged row of position p of sequence b (p counted from the start of the
+ * sequence), or -1 (past the table, or page outside [0, dim0)). */
+static int64_t orc_paged_position(int b, int64_t p, int dim0, int page_size,
+                                  const int32_t* block_table, int bt_cols)
+{
+    int64_t pi = p / page_size;
+    if (pi >= bt_cols) return -1;
+    int64_t page = block_table[(int64_t)b * bt_cols + pi];
+    if (page < 0 || page >= dim0) return -1;
+    return page * page_size + p % page_size;
+}
+
+/* Rows of the full prefix of each sequence: positions
+ * p in [0, min(cache_seqlens[b] + width, max_len)), in (b, p) order, with
+ * -1 for skipped positions; returns their count. */
+int64_t orc_prefix_rows(int dim0, int page_size, int batch_size, int width, int max_len,
+                        const int32_t* cache_seqlens, const int32_t* block_table, int bt_cols,
+                        int64_t* rows)
+{
+    int64_t n = 0;
+    for (int b = 0; b < batch_size; ++b) {
+        int64_t end = (int64_t)cache_seqlens[b] + width;
+        if (end > max_len) end = max_len;
+        for (int64_t p = 0; p < end; ++p)
+            rows[n++] = orc_paged_position(b, p, dim0, page_size, block_table, bt_cols);
+    }
+    return n;
+}
+
+void orc_kv_to_fp16_prefix(const uint8_t* k_in, uint16_t* k_out, const uint16_t* k_scales, int fmt_k,
+                           const uint8_t* v_in, uint16_t* v_out, const uint16_t* v_scales, int fmt_v,
+                           int dim0, int dim1, int heads, int head_dim,
+                           int batch_size, int width, int max_len,
+                           const int32_t* cache_seqlens, const int32_t* block_table, int bt_cols)
+{
+    const int64_t R = (int64_t)heads * head_dim;
+    for (int b = 0; b < batch_size; ++b) {
+        int64_t end = (int64_t)cache_seqlens[b] + width;
+        if (end > max_len) end = max_len;
+        for (int64_t p = 0; p < end; ++p) {
+            int64_t row = orc_paged_position(b, p, dim0, dim1, block_table, bt_cols);
+            if (row < 0) continue;
+            orc_widen_kv_row(row, R, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v);
+        }
+    }
+}
+
+/* Bytes one token occupies in one cache tensor of a format:
+ * 16 = fp16, 0 = 8-bit high byte, 4/6/8 = block codes + one fp16 per 32. */
+int64_t orc_bytes_per_token(int fmt, int heads, int head_dim)
+{
+    const int64_t R = (int64_t)heads * head_dim;
+    if (fmt == 16) return 2 * R;
+    return orc_fmt_row_bytes(R, fmt) + 2 * orc_fmt_scale_count(R, fmt);
+}

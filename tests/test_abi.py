@@ -179,3 +179,60 @@ def test_count_match_torch_inputs():
     assert kvq.kvq_count_match(a, b, 1000) == 37
     with pytest.raises(TypeError):
         kvq.kvq_count_match(a, b.to(torch.int32), 10)
+
+
+# ---------------------------------------------------------------- per-tensor formats, prefix, capacity
+def kv(lib, to_compact=True, k=(A, A + GB, A + 2 * GB), fk=4, v=(A + 3 * GB, A + 4 * GB, A + 5 * GB), fv=4,
+       s=None, batch=2, offset=0, width=4, page_size=0, sl=None, bt=None, cols=0):
+    fn = lib.kvq_fp16_to_kv if to_compact else lib.kvq_kv_to_fp16
+    return fn(k[0], k[1], k[2], fk, v[0], v[1], v[2], fv, s or shp(), batch, offset, width, page_size,
+              sl, bt, cols, None)
+
+
+def test_per_tensor_validation(lib):
+    assert kv(lib, fk=5) == WBITS
+    assert kv(lib, fv=16) == WBITS
+    assert kv(lib, fk=0) == NULL                                     # 8-bit with a scales pointer
+    assert kv(lib, fk=0, k=(A, A + GB, None), width=0) == 0          # 8-bit without scales: fine
+    assert kv(lib, fk=4, k=(A, A + GB, None)) == NULL                # block format needs scales
+    assert kv(lib, k=(A, None, None)) == NULL                        # partial
+    assert kv(lib, k=(None, None, A + 2 * GB)) == NULL               # scales of an absent tensor
+    assert kv(lib, k=(None, None, None), v=(None, None, None)) == NULL
+    assert kv(lib, k=(None, None, None), fk=99, width=0) == 0         # absent tensor: format ignored
+    assert kv(lib, s=shp(d=48)) == SHAPE
+    assert kv(lib, batch=5) == RANGE
+    assert kv(lib, k=(A, A, A + 2 * GB)) == OVERLAP
+    assert kv(lib, to_compact=False, fk=0, k=(A, A + GB, None), fv=6, width=0) == 0
+    assert kv(lib, page_size=16, sl=A + 6 * GB, bt=A + 7 * GB, cols=0) == RANGE
+    assert kv(lib, page_size=16, sl=A + 6 * GB, bt=A + 7 * GB, cols=4, width=0) == 0
+
+
+def test_prefix_validation(lib):
+    f = lib.kvq_kv_to_fp16_prefix
+
+    def call(k=(A, A + GB, A + 2 * GB), fk=4, batch=2, width=1, max_len=64, sl=A + 6 * GB, bt=A + 7 * GB, cols=4, s=None):
+        return f(k[0], k[1], k[2], fk, None, None, None, 0, s or shp(), batch, width, max_len, sl, bt, cols, None)
+
+    assert call(max_len=-1) == RANGE
+    assert call(cols=0) == RANGE
+    assert call(width=-1) == RANGE
+    assert call(sl=None) == NULL
+    assert call(fk=3) == WBITS
+    assert call(s=shp(d=40)) == SHAPE
+    assert call(max_len=0) == 0
+    assert call(batch=0) == 0
+
+
+def test_bytes_per_token_closed_form(lib):
+    for heads, head_dim in ((8, 128), (32, 128), (1, 32), (4, 64)):
+        R = heads * head_dim
+        assert kvq.kvq_bytes_per_token(kvq.KVQ_FMT_FP16, heads, head_dim) == 2 * R
+        assert kvq.kvq_bytes_per_token(kvq.KVQ_FMT_FP8, heads, head_dim) == R
+        assert kvq.kvq_bytes_per_token(kvq.KVQ_FMT_Q4, heads, head_dim) == R // 2 + R // 16
+        assert kvq.kvq_bytes_per_token(kvq.KVQ_FMT_Q6, heads, head_dim) == 3 * R // 4 + R // 16
+        assert kvq.kvq_bytes_per_token(kvq.KVQ_FMT_Q8, heads, head_dim) == R + R // 16
+        for fmt in (0, 4, 6, 8, 16):
+            assert kvq.kvq_bytes_per_token(fmt, heads, head_dim) == oracle.bytes_per_token(fmt, heads, head_dim)
+    assert lib.kvq_bytes_per_token(5, 8, 128) == WBITS
+    assert lib.kvq_bytes_per_token(4, 8, 48) == SHAPE
+    assert lib.kvq_bytes_per_token(16, 0, 128) == SHAPE

@@ -204,3 +204,135 @@ def test_count_match_bruteforce_vs_numpy(dtype):
                 diff = np.nonzero(a[:n] != b[:n])[0]
                 want = int(diff[0]) if diff.size else n
                 assert oracle.count_match(a, b, max_a) == want
+
+
+# ---------------------------------------------------------------- per-tensor formats, prefix, capacity
+FMTS = (0, 4, 6, 8)
+
+
+def _compact_np(shape, fmt):
+    d0, d1, h, d = shape
+    return _sentinel_like((d0, d1, h, d if fmt == 0 else d * fmt // 8), np.uint8)
+
+
+def _scales_np(shape, fmt):
+    if fmt == 0:
+        return None
+    d0, d1, h, d = shape
+    return _sentinel_like((d0, d1, h, d // 32), np.float16)
+
+
+def _paged_setup(rng, num_pages=20, page_size=4, B=3, cols=4):
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = perm[:B * cols].reshape(B, cols).copy()
+    bt[1, 3] = -1                                    # an invalid entry
+    sl = np.array([1, 6, 9], np.int32)[:B]
+    return bt, sl
+
+
+@pytest.mark.parametrize("fmt_k,fmt_v", [(0, 0), (0, 4), (4, 6), (6, 8), (8, 0)])
+def test_per_tensor_formats_paged(fmt_k, fmt_v):
+    """Each tensor in its own format equals the pinned single-format
+    conversion of that tensor (block formats) or the fp16 memory image's high
+    bytes (8-bit), on the rows the block-table expansion gives."""
+    rng = np.random.default_rng(71 + fmt_k * 10 + fmt_v)
+    page_size, num_pages, B, cols = 4, 20, 3, 4
+    shape = (num_pages, page_size, H, D)
+    k = (rng.standard_normal(shape) * 2).astype(np.float16)
+    v = (rng.standard_normal(shape) * 0.3).astype(np.float16)
+    bt, sl = _paged_setup(rng, num_pages, page_size, B, cols)
+    width = 7
+    kc, vc = _compact_np(shape, fmt_k), _compact_np(shape, fmt_v)
+    ks, vs = _scales_np(shape, fmt_k), _scales_np(shape, fmt_v)
+    oracle.fp16_to_kv(k, kc, ks, fmt_k, v, vc, vs, fmt_v, B, 0, width, page_size, sl, bt)
+    touched = set()
+    for b in range(B):
+        lay = _paged_positions(bt[b], page_size, cols * page_size)
+        for t in range(width):
+            p = int(sl[b]) + t
+            if p < len(lay) and lay[p] is not None and 0 <= lay[p][0] < num_pages:
+                touched.add(lay[p])
+    for x, c, sc, fmt in ((k, kc, ks, fmt_k), (v, vc, vs, fmt_v)):
+        for pg in range(num_pages):
+            for sl_ in range(page_size):
+                if (pg, sl_) not in touched:
+                    assert (c[pg, sl_] == 0xA5).all()
+                    continue
+                row = x[pg, sl_].reshape(1, -1)
+                if fmt == 0:
+                    assert (c[pg, sl_].reshape(-1) == row.view(np.uint8)[0, 1::2]).all()
+                else:
+                    codes, scales = oracle.quant_rows(row, fmt)
+                    assert (c[pg, sl_].reshape(-1) == codes[0]).all()
+                    assert (sc[pg, sl_].reshape(-1).view(np.uint16) == scales[0]).all()
+    # and back
+    ko, vo = _sentinel_like(shape, np.float16), _sentinel_like(shape, np.float16)
+    oracle.kv_to_fp16(kc, ko, ks, fmt_k, vc, vo, vs, fmt_v, B, 0, width, page_size, sl, bt)
+    for x, c, sc, o, fmt in ((k, kc, ks, ko, fmt_k), (v, vc, vs, vo, fmt_v)):
+        for (pg, sl_) in touched:
+            if fmt == 0:
+                want = x[pg, sl_].reshape(-1).view(np.uint16) & 0xFF00
+            else:
+                want = oracle.dequant_rows(c[pg, sl_].reshape(1, -1), sc[pg, sl_].reshape(1, -1).view(np.uint16), fmt)[0]
+            assert (o[pg, sl_].reshape(-1).view(np.uint16) == want).all()
+
+
+def test_prefix_rows_by_enumeration():
+    rng = np.random.default_rng(81)
+    for page_size in (1, 3, 4):
+        num_pages, B, cols = 30, 4, 5
+        bt = rng.integers(-1, num_pages + 2, size=(B, cols)).astype(np.int32)
+        sl = rng.integers(0, cols * page_size, size=B).astype(np.int32)
+        for width, max_len in ((0, 100), (2, 100), (3, 7), (1, 0)):
+            rows = oracle.prefix_rows(num_pages, page_size, B, width, max_len, sl, bt)
+            want = []
+            for b in range(B):
+                lay = _paged_positions(bt[b], page_size, cols * page_size)
+                for p in range(min(int(sl[b]) + width, max_len)):
+                    ok = p < len(lay) and lay[p] is not None and 0 <= lay[p][0] < num_pages
+                    want.append(lay[p][0] * page_size + lay[p][1] if ok else -1)
+            assert rows.tolist() == want
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_prefix_widen_touches_exactly_the_prefix(fmt):
+    rng = np.random.default_rng(91 + fmt)
+    page_size, num_pages, B, cols = 4, 20, 3, 4
+    shape = (num_pages, page_size, H, D)
+    x = (rng.standard_normal(shape)).astype(np.float16)
+    bt, sl = _paged_setup(rng, num_pages, page_size, B, cols)
+    c, sc = _compact_np(shape, fmt), _scales_np(shape, fmt)
+    # fill every row's compact form first (all rows valid input for widening)
+    allrows = x.reshape(-1, H * D)
+    if fmt == 0:
+        c[...] = x.view(np.uint8)[..., 1::2]
+    else:
+        codes, scales = oracle.quant_rows(allrows, fmt)
+        c.reshape(num_pages * page_size, -1)[...] = codes
+        sc.reshape(num_pages * page_size, -1).view(np.uint16)[...] = scales
+    out = _sentinel_like(shape, np.float16)
+    width, max_len = 2, 14
+    oracle.kv_to_fp16_prefix(c, out, sc, fmt, None, None, None, 0, B, width, max_len, sl, bt)
+    rows = oracle.prefix_rows(num_pages, page_size, B, width, max_len, sl, bt)
+    valid = set(int(r) for r in rows if r >= 0)
+    flat_out = out.reshape(num_pages * page_size, -1).view(np.uint16)
+    for r in range(num_pages * page_size):
+        if r not in valid:
+            assert (flat_out[r].view(np.uint8) == 0xA5).all()
+        elif fmt == 0:
+            assert (flat_out[r] == (allrows[r].view(np.uint16) & 0xFF00)).all()
+        else:
+            want = oracle.dequant_rows(c.reshape(num_pages * page_size, -1)[r:r + 1],
+                                       sc.reshape(num_pages * page_size, -1)[r:r + 1].view(np.uint16), fmt)
+            assert (flat_out[r] == want[0]).all()
+
+
+@pytest.mark.parametrize("heads,head_dim", [(8, 128), (1, 32), (3, 96)])
+def test_bytes_per_token_equals_output_sizes(heads, head_dim):
+    R = heads * head_dim
+    x = np.zeros((1, R), np.float16)
+    assert oracle.bytes_per_token(16, heads, head_dim) == x.nbytes
+    assert oracle.bytes_per_token(0, heads, head_dim) == x.view(np.uint8)[:, 1::2].nbytes
+    for fmt in (4, 6, 8):
+        codes, scales = oracle.quant_rows(x, fmt)
+        assert oracle.bytes_per_token(fmt, heads, head_dim) == codes.nbytes + scales.nbytes
