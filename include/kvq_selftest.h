@@ -45,6 +45,15 @@ KVQ_API int kvq_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s1
 KVQ_API int kvq_selftest_scales(const uint16_t* absmax, int64_t n, int wbits, uint16_t* out,
                         void* hip_stream);
 
+/*
+ * q[i] = n[i] / d (integer division) through the multiply-shift divider the
+ * kernels use to split logical rows into (sequence, token) and positions
+ * into (page, slot).  n[i] < 2^31, 1 <= d < 2^31; device pointers, 4-byte
+ * aligned.  KVQ_ERR_RANGE for d or count out of range.
+ */
+KVQ_API int kvq_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, uint32_t* q,
+                                 void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

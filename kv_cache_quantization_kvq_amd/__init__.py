@@ -21,7 +21,7 @@ from . import _build
 
 __all__ = ["KvqError", "kvq_fp16_to_fp8", "kvq_fp8_to_fp16", "kvq_fp16_to_q_kv",
            "kvq_q_to_fp16_kv", "kvq_count_match", "kvq_strerror", "kvq_version",
-           "kvq_selftest_codes", "kvq_selftest_scales", "library_path", "load_library",
+           "kvq_selftest_codes", "kvq_selftest_scales", "kvq_selftest_fastdiv", "library_path", "load_library",
            "code_shape", "scale_shape", "kvq_fp16_to_kv", "kvq_kv_to_fp16", "kvq_kv_to_fp16_prefix",
            "kvq_bytes_per_token", "compact_shape", "KVQ_FMT_FP8", "KVQ_FMT_Q4", "KVQ_FMT_Q6",
            "KVQ_FMT_Q8", "KVQ_FMT_FP16"]
@@ -75,6 +75,7 @@ def load_library():
             "kvq_version": (_i, []),
             "kvq_selftest_codes": (_i, [_vp, _i64, _vp, _i64, _i, _i, _vp, _vp]),
             "kvq_selftest_scales": (_i, [_vp, _i64, _i, _vp, _vp]),
+            "kvq_selftest_fastdiv": (_i, [_vp, _i64, ctypes.c_uint32, _vp, _vp]),
             "kvq_fp16_to_kv": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, Shape, _i, _i, _i, _i,
                                     _vp, _vp, _i, _vp]),
             "kvq_kv_to_fp16": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, Shape, _i, _i, _i, _i,
@@ -400,3 +401,15 @@ def kvq_selftest_scales(a_bits, wbits, out, stream=None):
     rc = load_library().kvq_selftest_scales(pa, a_bits.numel(), int(wbits), po,
                                             _stream_handle(stream, dev))
     _check(rc, "kvq_selftest_scales")
+
+
+def kvq_selftest_fastdiv(n, d, out, stream=None):
+    """out[i] = n[i] // d through the kernels' multiply-shift divider (device
+    int32 tensors, 0 <= n < 2^31, 1 <= d < 2^31)."""
+    torch = _torch()
+    dev = n.device
+    pn = _dev_ptr(n, "n", torch.int32)
+    po = _dev_ptr(out, "out", torch.int32, dev)
+    _expect_shape(out, tuple(n.shape), "out")
+    rc = load_library().kvq_selftest_fastdiv(pn, n.numel(), int(d), po, _stream_handle(stream, dev))
+    _check(rc, "kvq_selftest_fastdiv")

@@ -327,4 +327,12 @@ int kvq_selftest_scales(const uint16_t* absmax, int64_t n, int wbits, uint16_t* 
     return kvq::launch_selftest_scales(absmax, n, wbits, out, hip_stream) ? KVQ_ERR_HIP : KVQ_OK;
 }
 
+int kvq_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, uint32_t* q, void* hip_stream) {
+    if (!n || !q) return KVQ_ERR_NULL;
+    if (d == 0 || d > (uint32_t)INT32_MAX || count < 0 || count > (int64_t)INT32_MAX * 64) return KVQ_ERR_RANGE;
+    if (!aligned(n, 4) || !aligned(q, 4)) return KVQ_ERR_ALIGN;
+    if (count == 0) return KVQ_OK;
+    return kvq::launch_selftest_fastdiv(n, count, d, q, hip_stream) ? KVQ_ERR_HIP : KVQ_OK;
+}
+
 }  // extern "C"

@@ -37,6 +37,28 @@ struct QLaunch {
     int32_t max_len;              // full-prefix calls: positions enumerated per sequence
 };
 
+// Division by a run-time constant d (1 <= d < 2^31) without a divide, for
+// numerators 0 <= n < 2^31 (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994, Theorem 4.2, with N = 32):
+//   l = ceil(log2 d),  m = floor(2^(32+l) / d) + 1 = 2^32 + mul,
+//   floor(n / d) = floor(m n / 2^(32+l)) = (mulhi(n, mul) + n) >> l.
+// The theorem needs 2^(32+l) <= m d <= 2^(32+l) + 2^l, which holds because
+// 2^(32+l) < m d <= 2^(32+l) + d and d <= 2^l; mulhi(n, mul) < n keeps the
+// sum below 2^32 for n < 2^31.
+struct FastDiv {
+    uint32_t mul;
+    uint32_t shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while (l < 31 && (1u << l) < d) ++l;
+    FastDiv f;
+    f.mul = (uint32_t)((((uint64_t)1 << l) - d) * ((uint64_t)1 << 32) / d + 1);
+    f.shift = l;
+    return f;
+}
+
 // Launchers (return a hipError_t value as int, 0 on success).
 int launch_fp16_to_fp8(const Fp8Launch& a, void* stream);
 int launch_fp8_to_fp16(const Fp8Launch& a, void* stream);
@@ -50,5 +72,6 @@ int launch_kv_to_fp16_prefix(const QLaunch& a, void* stream);
 int launch_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s, int64_t ns,
                           int wbits, bool force_clamp, uint8_t* u, void* stream);
 int launch_selftest_scales(const uint16_t* a, int64_t n, int wbits, uint16_t* out, void* stream);
+int launch_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, uint32_t* q, void* stream);
 
 }  // namespace kvq

@@ -28,17 +28,19 @@ constexpr int kFp8Cpt = 4;                // chunks per thread, 8-bit kernels
 
 // ---------------------------------------------------------------- memory policy
 //
-// Data read once or written for later use elsewhere are accessed with the
-// non-temporal hint ("nt": streamed through the caches with low retention):
-// the source of every conversion (fp16 rows to quantize or narrow, codes,
-// scales and bytes to widen back) and the fp16 rows written by dequantize
-// and by 8-bit -> fp16.  The compact outputs (codes, scales, 8-bit bytes) use
-// ordinary stores, so an immediately following inverse conversion of the
-// same rows finds them in cache.  (Measured on MI355X at the paged Q4
-// workload: a quantize + dequantize step goes from 23.5 us with ordinary
-// accesses to 19.6 us.)
+// Every conversion streams: its sources (fp16 rows to quantize or narrow,
+// codes, scales and bytes to widen back) are loaded, and all of its outputs
+// stored, with the non-temporal hint ("nt": streamed through the caches with
+// low retention).  A kernel's dirty L2 lines are written back when it ends,
+// so outputs that stream out during the kernel shorten its tail.  Measured
+// on MI355X at the paged Q4 workload (43 MB per launch, cold rows), against
+// ordinary stores: quantize 10.9 -> 10.2 us, dequantize 12.4 -> 11.0 us, and
+// a quantize + dequantize step 21.9 -> 21.2 us; the device-scope (sc0/sc1)
+// write-through policies were slower per kernel.
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x3_t __attribute__((ext_vector_type(3), aligned(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 ld_nt(const uint4* p) {
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -50,8 +52,32 @@ __device__ __forceinline__ void st_nt(uint4* p, uint4 v) {
     const u32x4_t w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
 }
+__device__ __forceinline__ void st_nt(uint2* p, uint2 v) {
+    const u32x2_t w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+}
+// 12 bytes at a 4-byte aligned address
+__device__ __forceinline__ void st_nt3(void* p, uint32_t a, uint32_t b, uint32_t c) {
+    const u32x3_t w = {a, b, c};
+    __builtin_nontemporal_store(w, static_cast<u32x3_t*>(p));
+}
+__device__ __forceinline__ void st_nt(uint16_t* p, uint32_t v) { __builtin_nontemporal_store((uint16_t)v, p); }
 
 // ---------------------------------------------------------------- row map
+
+struct QGeom {
+    int32_t n_units;   // rows * ntens * nseg
+    int32_t nseg;      // row segments per row
+    int32_t ntens;     // tensors present: 1 or 2
+    int32_t tens0;     // the tensor when ntens == 1: 0 = K, 1 = V
+    FastDiv seq_div;   // logical rows per sequence: width (max_len for kPrefix)
+    FastDiv page_div;  // page_size (paged modes)
+};
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+    return (__umulhi(n, f.mul) + n) >> f.shift;
+}
+
 
 // How logical rows map to cache rows.
 enum RowMode {
@@ -63,11 +89,12 @@ enum RowMode {
 // Physical row of logical row n, or -1 when skipped.  Paged positions p live
 // in page block_table[b][p / page_size], slot p % page_size, and are skipped
 // if p < 0, past the table, or the page is outside [0, dim0).  All values
-// are wave-uniform (scalar loads and SALU).
+// are wave-uniform (scalar loads and SALU).  The host bounds n and
+// bt_cols * page_size below 2^31, the domain of fast_div.
 template <int MODE>
-__device__ __forceinline__ int64_t resolve_row(const QLaunch& a, int32_t n) {
+__device__ __forceinline__ int64_t resolve_row(const QLaunch& a, const QGeom& g, int32_t n) {
     const int32_t per_seq = MODE == kPrefix ? a.max_len : a.width;
-    const int32_t b = n / per_seq;
+    const int32_t b = (int32_t)fast_div((uint32_t)n, g.seq_div);
     const int32_t t = n - b * per_seq;
     if (MODE == kContig) return (int64_t)b * a.dim1 + a.offset + t;
     int64_t p;
@@ -80,7 +107,7 @@ __device__ __forceinline__ int64_t resolve_row(const QLaunch& a, int32_t n) {
     }
     if (p >= (int64_t)a.bt_cols * a.page_size) return -1;
     const uint32_t pu = (uint32_t)p;
-    const uint32_t pi = pu / (uint32_t)a.page_size;
+    const uint32_t pi = fast_div(pu, g.page_div);
     const int32_t page = a.block_table[(int64_t)b * a.bt_cols + pi];
     if (page < 0 || page >= a.dim0) return -1;
     return (int64_t)page * a.page_size + (int64_t)(pu - pi * (uint32_t)a.page_size);
@@ -93,12 +120,6 @@ __device__ __forceinline__ int64_t resolve_row(const QLaunch& a, int32_t n) {
 // then the row, so neighbouring waves share the row's paging lookup and
 // touch neighbouring memory.  One wavefront converts one unit.
 
-struct QGeom {
-    int32_t n_units;   // rows * ntens * nseg
-    int32_t nseg;      // row segments per row
-    int32_t ntens;     // tensors present: 1 or 2
-    int32_t tens0;     // the tensor when ntens == 1: 0 = K, 1 = V
-};
 
 struct UnitRef {
     int64_t row;       // physical row (0 for a padding or skipped unit)
@@ -129,7 +150,7 @@ __device__ __forceinline__ UnitRef unit_ref(const QLaunch& a, const QGeom& g, in
         n = rt;
         r.tensor = g.tens0;
     }
-    const int64_t row = resolve_row<MODE>(a, n);
+    const int64_t row = resolve_row<MODE>(a, g, n);
     r.live = r.live && row >= 0;
     r.row = row >= 0 ? row : 0;
     return r;
@@ -178,23 +199,21 @@ __device__ __forceinline__ void quant_unit(const QLaunch& a, const UnitRef& ur, 
     uint8_t* codes = static_cast<uint8_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * (int64_t)(R / 8 * WBITS);
     if constexpr (WBITS == 4) {
         const uint2 d = make_uint2(pack_q4(u0), pack_q4(u1));
-        if (store) *reinterpret_cast<uint2*>(codes + 8 * pc) = d;
+        if (store) st_nt(reinterpret_cast<uint2*>(codes + 8 * pc), d);
     } else if constexpr (WBITS == 8) {
         const uint4 d = make_uint4(pack_q8x4(u0[0], u0[1], u0[2], u0[3]), pack_q8x4(u0[4], u0[5], u0[6], u0[7]),
                                    pack_q8x4(u1[0], u1[1], u1[2], u1[3]), pack_q8x4(u1[4], u1[5], u1[6], u1[7]));
-        if (store) *reinterpret_cast<uint4*>(codes + 16 * pc) = d;
+        if (store) st_nt(reinterpret_cast<uint4*>(codes + 16 * pc), d);
     } else {
         uint32_t lo0, hi0, lo1, hi1;
         pack_q6(u0, lo0, hi0);
         pack_q6(u1, lo1, hi1);
-        uint32_t d[3];
-        d[0] = lo0;
-        d[1] = __builtin_amdgcn_perm(lo1, hi0, 0x05040100u);   // hi0.lo16 | lo1.lo16 << 16
-        d[2] = __builtin_amdgcn_alignbit(hi1, lo1, 16);        // lo1 >> 16 | hi1 << 16
-        if (store) __builtin_memcpy(codes + 12 * pc, d, 12);    // 4-byte aligned
+        const uint32_t d1 = __builtin_amdgcn_perm(lo1, hi0, 0x05040100u);   // hi0.lo16 | lo1.lo16 << 16
+        const uint32_t d2 = __builtin_amdgcn_alignbit(hi1, lo1, 16);        // lo1 >> 16 | hi1 << 16
+        if (store) st_nt3(codes + 12 * pc, lo0, d1, d2);
     }
     uint16_t* scales = static_cast<uint16_t*>(ur.tensor ? a.v_scales : a.k_scales) + ur.row * (int64_t)(R >> 5);
-    if (store && (lane & 1) == 0) scales[pc >> 1] = (uint16_t)s16;
+    if (store && (lane & 1) == 0) st_nt(scales + (pc >> 1), s16);
 }
 
 // high byte of each fp16: bytes 1,3 of the first word then 1,3 of the second
@@ -212,7 +231,7 @@ __device__ __forceinline__ void narrow_unit(const QLaunch& a, const UnitRef& ur,
     const uint4 d = make_uint4(high_bytes(x0.x, x0.y), high_bytes(x0.z, x0.w),
                                high_bytes(x1.x, x1.y), high_bytes(x1.z, x1.w));
     uint8_t* out = static_cast<uint8_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * (int64_t)a.R;
-    if (ur.live && in) *reinterpret_cast<uint4*>(out + 16 * pc) = d;
+    if (ur.live && in) st_nt(reinterpret_cast<uint4*>(out + 16 * pc), d);
 }
 
 template <int WBITS, int MODE, bool GUARD>
@@ -378,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void fp16_to_fp8_kernel(Fp8Launch a) {
 #pragma unroll
         for (int k = 0; k < kFp8Cpt; ++k) {
             const int64_t c = c0 + k * kThreads;
-            if (c < cps) dst[c] = make_uint2(high_bytes(v[k].x, v[k].y), high_bytes(v[k].z, v[k].w));
+            if (c < cps) st_nt(dst + c, make_uint2(high_bytes(v[k].x, v[k].y), high_bytes(v[k].z, v[k].w)));
         }
     }
 }
@@ -438,6 +457,12 @@ __global__ __launch_bounds__(kThreads) void selftest_scales_kernel(const uint16_
                                                                    uint16_t* __restrict__ out) {
     const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (t < n) out[t] = (uint16_t)scale_from_absmax<WBITS>(a[t]);
+}
+
+__global__ __launch_bounds__(kThreads) void selftest_fastdiv_kernel(const uint32_t* __restrict__ n, int64_t count,
+                                                                      FastDiv f, uint32_t* __restrict__ q) {
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t < count) q[t] = fast_div(n[t], f);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -530,6 +555,8 @@ static int launch_units(const QLaunch& a, bool to_compact, bool mixed, int mode,
     g.ntens = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
     g.tens0 = a.k_src ? 0 : 1;
     g.n_units = (int32_t)(rows * g.ntens * g.nseg);   // bounded by the host checks
+    g.seq_div = make_fastdiv((uint32_t)(mode == kPrefix ? a.max_len : a.width));
+    g.page_div = make_fastdiv(a.page_size > 0 ? (uint32_t)a.page_size : 1u);
     const dim3 grid((unsigned)((g.n_units + kWaves - 1) / kWaves));
     QLaunch arg = a;
     void* args[] = {&arg, &g};
@@ -586,6 +613,13 @@ int launch_selftest_scales(const uint16_t* a, int64_t n, int wbits, uint16_t* ou
                    : wbits == 6 ? reinterpret_cast<const void*>(&selftest_scales_kernel<6>)
                                 : reinterpret_cast<const void*>(&selftest_scales_kernel<8>);
     return launch(fn, grid, dim3(kThreads), args, stream);
+}
+
+int launch_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, uint32_t* q, void* stream) {
+    FastDiv f = make_fastdiv(d);
+    dim3 grid((unsigned)((count + kThreads - 1) / kThreads));
+    void* args[] = {&n, &count, &f, &q};
+    return launch(reinterpret_cast<const void*>(&selftest_fastdiv_kernel), grid, dim3(kThreads), args, stream);
 }
 
 }  // namespace kvq

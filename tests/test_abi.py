@@ -102,6 +102,18 @@ def test_q_validation(lib):
     assert q(lib, quant=False, k=(A, A, A + 2 * GB)) == OVERLAP
 
 
+def test_selftest_fastdiv_validation(lib):
+    f = lib.kvq_selftest_fastdiv
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(A, 16, 0, A + GB, None) == RANGE
+    assert f(A, 16, 1 << 31, A + GB, None) == RANGE
+    assert f(A, -1, 7, A + GB, None) == RANGE
+    assert f(None, 16, 7, A + GB, None) == NULL
+    assert f(A + 2, 16, 7, A + GB, None) == ALIGN
+    assert f(A, 0, 7, A + GB, None) == 0
+
+
 def test_q_zero_work_returns_ok(lib):
     # valid arguments but nothing to do: no launch, success
     assert q(lib, width=0) == 0

@@ -91,6 +91,39 @@ def test_code_rule_exhaustive(kvq, wbits):
     pool.shutdown()
 
 
+def _fastdiv_divisors():
+    d = set(range(1, 4097))
+    for k in range(1, 31):
+        d.update({(1 << k) - 1, 1 << k, (1 << k) + 1})
+    d.update({(1 << 31) - 1, 256, 512, 4096 * 256, 65280, 7937})
+    rng = np.random.default_rng(5150)
+    d.update(int(x) for x in rng.integers(4097, 1 << 31, size=200))
+    return sorted(x for x in d if 1 <= x < (1 << 31))
+
+
+def test_fastdiv_divider(kvq):
+    """The kernels' multiply-shift row splitter vs integer division: every
+    divisor 1..4096, 2^k - 1 / 2^k / 2^k + 1 up to 2^31 - 1, the workload
+    divisors and 200 random ones; numerators at every multiple's edges up to
+    64 d, the top of the domain and random values below 2^31."""
+    t = torch()
+    rng = np.random.default_rng(5151)
+    top = (1 << 31) - 1
+    rand = rng.integers(0, 1 << 31, size=2048, dtype=np.int64)
+    for d in _fastdiv_divisors():
+        k = np.arange(0, 65, dtype=np.int64) * d
+        n = np.concatenate([k - 1, k, k + 1, [top, top - 1, top - d, top - d + 1], rand])
+        n = np.unique(n[(n >= 0) & (n <= top)])
+        nd = t.from_numpy(n.astype(np.int32)).cuda()
+        out = t.empty_like(nd)
+        kvq.kvq_selftest_fastdiv(nd, d, out)
+        got = host(out).astype(np.int64)
+        want = n // d
+        if not np.array_equal(got, want):
+            i = int(np.argmax(got != want))
+            raise AssertionError("fastdiv: %d // %d gave %d" % (n[i], d, got[i]))
+
+
 @pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_dequant_exhaustive_through_kernel(kvq, wbits):
     """Every (code, scale) pair for all finite scales >= 0 through the
