@@ -91,7 +91,8 @@ class PagedKV:
         self.rows_per_launch = 2 * w.batch_size * w.width            # K and V rows
         self.bytes_per_launch = self.rows_per_launch * q_row_bytes(wbits)
         self.bytes_per_step = 2 * self.bytes_per_launch
-        self.elems_per_step = 2 * self.rows_per_launch * ROW
+        self.elems_per_launch = self.rows_per_launch * ROW
+        self.elems_per_step = 2 * self.elems_per_launch
 
     def quant(self, d):
         sl, bt = self.tables[d]
@@ -175,6 +176,41 @@ def cpu_baseline(wl, oracle, rows_fn, draws):
     n_rows = sum(g[2].size for g in groups)
     return {"seconds": dt, "threads": threads, "rows": n_rows,
             "bytes": n_rows * q_row_bytes(4) * 2, "groups": per_group}
+
+
+def oracle_detail(wl, oracle, rows_fn, kvq):
+    """Single-thread oracle rate on one draw's rows, and the naive oracle
+    count_match beside the library's 64-bit-chunk scan (same ids)."""
+    sl, bt = wl.w.extra["tables"][0]
+    rows = oracle.call_rows(wl.w.shape[0], wl.w.shape[1], wl.w.batch_size, wl.w.offset,
+                            wl.w.width, wl.w.page_size, sl, bt)
+    rows = rows[rows >= 0]
+    x = rows_fn(wl.k, rows)
+    t0 = time.perf_counter()
+    c, s = oracle.quant_rows(x, 4)
+    oracle.dequant_rows(c, s, 4)
+    dt = time.perf_counter() - t0
+    from kv_cache_quantization_kvq_amd import synth
+    mw = synth.mix_paged()
+    a, b = mw.extra["ids_a"], mw.extra["ids_b"]
+    reps = 20
+    t1 = time.perf_counter()
+    for _ in range(reps):
+        m_oracle = oracle.count_match(a, b, a.size)
+    t_or = (time.perf_counter() - t1) / reps
+    t1 = time.perf_counter()
+    for _ in range(reps):
+        m_lib = kvq.kvq_count_match(a, b, a.size)
+    t_lib = (time.perf_counter() - t1) / reps
+    if m_oracle != m_lib:
+        log("count_match mismatch: oracle %d, library %d" % (m_oracle, m_lib))
+        sys.exit(4)
+    return {"single_thread": {"GB/s": round(rows.size * q_row_bytes(4) * 2 / dt / 1e9, 4),
+                              "elements_per_s": round(rows.size * ROW * 2 / dt, 1),
+                              "sample": "%d K rows of one paged-Q4 step quantized then dequantized, 1 thread"
+                                        % rows.size},
+            "count_match": {"n": int(a.size), "match": m_lib, "oracle_us": round(t_or * 1e6, 2),
+                            "library_us": round(t_lib * 1e6, 2)}}
 
 
 def main():
@@ -262,6 +298,12 @@ def main():
                 "kernel": ("quant_kv_kernel<4>" if dom == "quant" else "dequant_kv_kernel<4>"),
                 "bytes_per_launch": wl.bytes_per_launch,
                 "avg_us": {k: round(v * 1e6, 3) for k, v in kt.items()}}
+    # the pair figure: algorithmic bytes of one quantize and one dequantize
+    # launch over the sum of their kernel times (cold rows, serial launches)
+    pair_s = kt["quant"] + kt["dequant"]
+    kernel_pair = {"us": round(pair_s * 1e6, 3), "GB/s": round(2 * wl.bytes_per_launch / pair_s / 1e9, 1),
+                   "frac": round(2 * wl.bytes_per_launch / pair_s / 1e9 / HBM_PEAK_GBS, 4),
+                   "elements_per_s": round(2 * wl.elems_per_launch / pair_s, 1)}
 
     # parity of the timed data: outputs of every draw against the oracle on a sample
     import oracle
@@ -272,7 +314,7 @@ def main():
         a = x.cpu().numpy()
         return a.view(np.uint16) if a.dtype == np.float16 else a
 
-    cpu = None
+    cpu = cpu_detail = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on %d draws" % args.cpu_draws)
         cb = cpu_baseline(wl, oracle, rows_fn, args.cpu_draws)
@@ -284,6 +326,7 @@ def main():
                 log("PARITY FAILURE on the timed data (draw %d, %s)" % (d, name))
                 sys.exit(4)
         log("timed data matches the oracle on %d rows" % cb["rows"])
+        cpu_detail = oracle_detail(wl, oracle, rows_fn, kvq)
         cpu = {"value": round(cb["bytes"] / cb["seconds"] / 1e9, 4), "unit": "GB/s", "cores": cb["threads"],
                "kind": "oracle",
                "sample": "%d rows (K and V of %d paged-Q4 steps) quantized then dequantized by the "
@@ -305,7 +348,9 @@ def main():
                       "bytes_per_step": wl.bytes_per_step,
                       "timed": ("graph, %d chains" % args.streams) if graphs else "eager",
                       "device": dev_name},
-           "roofline": roofline, "cpu_baseline": cpu}
+           "roofline": roofline, "kernel_pair": kernel_pair, "cpu_baseline": cpu}
+    if cpu_detail is not None:
+        rec["cpu_detail"] = cpu_detail
     if secondary is not None:
         rec["secondary"] = secondary
     print(json.dumps(rec), flush=True)
@@ -350,6 +395,11 @@ def secondary_workloads(torch, kvq, synth, wl):
     out = {}
     w = wl.w
     rows = w.batch_size * w.width
+    # the same paged-Q4 launches with one draw repeated (rows and tables
+    # cache-resident): context only
+    kt = time_kernels(t, [("quant", wl.quant, [0]), ("dequant", wl.dequant, [0])], 4 * DRAWS)
+    out["paged_q4_hot"] = {k: {"us": round(v * 1e6, 2), "GB/s": round(wl.bytes_per_launch / v / 1e9, 1)}
+                           for k, v in kt.items()}
     # other block widths on the paged workload
     for wb in (6, 8):
         other = PagedKV(torch, kvq, synth, wbits=wb, share=wl)
