@@ -114,6 +114,19 @@ def test_selftest_fastdiv_validation(lib):
     assert f(A, 0, 7, A + GB, None) == 0
 
 
+def test_size_bounds(lib):
+    """Rows up to 2^20 elements are accepted, longer ones are SHAPE; a call
+    whose work units exceed the 32-bit numbering is RANGE (checked before any
+    launch: batch 0 returns without one)."""
+    assert q(lib, s=shp(d0=1, d1=2, h=8192, d=128), batch=0, width=2) == 0
+    assert q(lib, s=shp(d0=1, d1=2, h=8193, d=128), batch=0, width=2) == SHAPE
+    assert q(lib, s=shp(d0=1 << 16, d1=1 << 15, h=8, d=128), batch=1 << 16, width=1 << 15) == RANGE
+    assert q(lib, s=shp(d0=1 << 16, d1=1 << 15, h=8, d=128), batch=1 << 16, width=1 << 15,
+             quant=False) == RANGE
+    f = lib.kvq_fp16_to_fp8
+    assert f(A, A + GB, shp(d0=1, d1=2, h=8193, d=128), 0, 0, 2, None) == SHAPE
+
+
 def test_q_zero_work_returns_ok(lib):
     # valid arguments but nothing to do: no launch, success
     assert q(lib, width=0) == 0

@@ -105,6 +105,20 @@ def test_per_tensor_contig_ragged(kvq, heads, head_dim, fmts):
         _roundtrip(kvq, k, v, fmts[0], fmts[1], batch, offset, width, what="contig %s %s" % (shape, fmts))
 
 
+@pytest.mark.parametrize("fmts", [(0, 6), (4, 8)])
+def test_max_row_length_paged(kvq, fmts):
+    """Rows of 2^20 elements through the per-tensor entry points on pages of
+    two tokens (a position crossing a page boundary)."""
+    rng = np.random.default_rng(2 ** 20 + 10 * fmts[0] + fmts[1])
+    shape = (3, 2, 8192, 128)
+    k = rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+    v = (rng.standard_normal(shape, dtype=np.float32) * 0.01).astype(np.float16)
+    bt = np.array([[2, 0]], np.int32)
+    sl = np.array([1], np.int32)
+    _log("max row paged %s %s" % (shape, fmts))
+    _roundtrip(kvq, k, v, fmts[0], fmts[1], 1, 0, 2, 2, sl, bt, what="max row paged %s" % (fmts,))
+
+
 def test_single_tensor_calls(kvq):
     t = torch()
     rng = np.random.default_rng(5)

@@ -172,6 +172,34 @@ def _contig_roundtrip(kvq, k, v, batch, offset, width, wbits, stream=None, what=
     byte_diff(host(vo), ovo.view(np.uint16), what + " V dequant")
 
 
+@pytest.mark.parametrize("wbits", [4, 6, 8])
+def test_max_row_length(kvq, wbits):
+    """The longest token row the library accepts: heads * head_dim = 2^20
+    elements (1024 segments of a row per tensor)."""
+    rng = np.random.default_rng(2 ** 20 + wbits)
+    shape = (2, 3, 8192, 128)
+    k = rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+    v = (rng.standard_normal(shape, dtype=np.float32) * 100).astype(np.float16)
+    _log("max row %s wbits %d" % (shape, wbits))
+    _contig_roundtrip(kvq, k, v, 2, 1, 2, wbits, what="max row")
+
+
+def test_max_row_length_fp8(kvq):
+    t = torch()
+    rng = np.random.default_rng(2 ** 20)
+    shape = (2, 3, 8192, 128)
+    x = rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+    o8 = sentinel(shape, t.uint8)
+    kvq.kvq_fp16_to_fp8(dev(x), o8, 2, 1, 2)
+    ob = sentinel(shape, t.float16)
+    kvq.kvq_fp8_to_fp16(o8, ob, 2, 1, 2)
+    w8, wb = sentinel_np(shape, np.uint8), sentinel_np(shape, np.float16)
+    oracle.fp16_to_fp8(x, w8, 2, 1, 2)
+    oracle.fp8_to_fp16(w8, wb, 2, 1, 2)
+    byte_diff(host(o8), w8, "max row 8-bit")
+    byte_diff(host(ob), wb.view(np.uint16), "max row widen")
+
+
 def test_q4_contig_workload(kvq):
     w = synth.q4_contig()
     _log("q4_contig %s offset %d width %d" % (w.shape, w.offset, w.width))
