@@ -375,7 +375,7 @@ def traffic_for(kernel, algo_bytes):
 
 def sources_digest():
     h = hashlib.sha256()
-    for f in ("kvq_kernels.hip", "kvq_device.h"):
+    for f in ("kvq_kernels.hip", "kvq_device.h", "kvq_internal.h"):
         with open(os.path.join(ROOT, "kv_cache_quantization_kvq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

@@ -6,7 +6,9 @@
  * sweep every fp16 (x, scale) pair against an independent reference.  The
  * arithmetic they expose is the block quantization of the ExLlamaV2 cache
  * page (Description of fp16_to_q_kv; I/O Contract: per-block scale factors,
- * wbits 4 or 6) with the numeric reading stated in kvq.h.
+ * wbits 4 or 6, plus 8 here) with the numeric reading stated in kvq.h, and
+ * the row split of the paged addressing (Description: block_table /
+ * cache_seqlens).
  * Same conventions as kvq.h: device pointers, asynchronous on hip_stream,
  * 0 or a negative KVQ_ERR_* code.
  */

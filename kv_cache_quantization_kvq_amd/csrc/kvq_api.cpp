@@ -44,8 +44,9 @@ bool any_output_overlap(const Extent* e, int n) {
     return false;
 }
 
-// Common shape/window checks.  `row_multiple` is the divisibility asked of
-// head_dim (Q paths) or of the row length (8-bit path).
+// Common shape/window checks.  q_path: head_dim % 32 == 0 (block formats
+// and the per-tensor calls); otherwise the row length % 8 == 0 (contiguous
+// 8-bit path).
 int check_shape(const kvq_shape& s, bool q_path) {
     if (s.dim0 <= 0 || s.dim1 <= 0 || s.heads <= 0 || s.head_dim <= 0) return KVQ_ERR_SHAPE;
     const int64_t R = (int64_t)s.heads * s.head_dim;
@@ -294,7 +295,7 @@ const char* kvq_strerror(int code) {
     switch (code) {
         case KVQ_OK: return "success";
         case KVQ_ERR_NULL: return "required pointer is NULL or a K/V triple is partial";
-        case KVQ_ERR_WBITS: return "wbits must be 4, 6 or 8";
+        case KVQ_ERR_WBITS: return "wbits must be 4, 6 or 8 (a format: KVQ_FMT_FP8, _Q4, _Q6 or _Q8)";
         case KVQ_ERR_SHAPE: return "invalid cache shape (head_dim % 32 for Q paths, heads*head_dim % 8 for 8-bit, page_size == dim1 when paged)";
         case KVQ_ERR_RANGE: return "size, offset or window out of range";
         case KVQ_ERR_ALIGN: return "device pointer not 16-byte aligned (int32 tables: 4)";

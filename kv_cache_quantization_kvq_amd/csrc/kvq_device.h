@@ -1,8 +1,9 @@
 // kvq_device.h -- gfx950 device building blocks of the KV-cache conversions.
 //
 // A "chunk" is 8 consecutive fp16 elements of a token row (one 128-bit
-// load).  Four consecutive lanes hold one 32-element quantization block, so
-// block reductions are DPP quad permutations inside a wave (no LDS).
+// load).  When quantizing, a lane holds two consecutive chunks and a lane
+// pair one 32-element block, so the block absmax is one DPP exchange inside
+// the wave (no LDS).
 //
 // Arithmetic definitions (ExLlamaV2 cache page, Description of fp16_to_q_kv /
 // q_to_fp16_kv; the numeric reading is stated in kvq.h):
@@ -37,39 +38,18 @@ __device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cas
 
 // ---------------------------------------------------------------- reductions
 
-// Largest |x| of the 8 fp16 values of a chunk, as fp16 bits.  For finite
-// values, ordering of |x| equals unsigned ordering of the bits with the sign
-// cleared, so this is packed u16 max on (bits & 0x7FFF).
-__device__ __forceinline__ uint32_t absmax_chunk(uint4 v) {
-    u16x2_t a = __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu);
-    u16x2_t b = __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu);
-    u16x2_t c = __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu);
-    u16x2_t d = __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu);
-    u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
-                                          __builtin_elementwise_max(c, d));
-    return (uint32_t)(m.x > m.y ? m.x : m.y);
-}
-
-// DPP quad_perm controls: [1,0,3,2] and [2,3,0,1].
-constexpr int kQuadSwap1 = 0xB1;
-constexpr int kQuadSwap2 = 0x4E;
-
-// Max over the 4 lanes of a quad (all four lanes of a quad are always
-// active together: a block never straddles a quad).
-__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
-    uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false);
-    v = v > o ? v : o;
-    o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap2, 0xF, 0xF, false);
-    return v > o ? v : o;
-}
+// DPP quad_perm control [1,0,3,2]: each lane reads its pair partner (lane ^ 1).
+constexpr int kPairSwap = 0xB1;
 
 // Max over a lane pair (lanes 2m, 2m+1), both active together.
 __device__ __forceinline__ uint32_t pair_max(uint32_t v) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kPairSwap, 0xF, 0xF, false);
     return v > o ? v : o;
 }
 
-// Largest |x| of the 16 fp16 values of two chunks, as fp16 bits.
+// Largest |x| of the 16 fp16 values of two chunks, as fp16 bits.  For
+// finite values, ordering of |x| equals unsigned ordering of the bits with
+// the sign cleared, so this is packed u16 max on (bits & 0x7FFF).
 __device__ __forceinline__ uint32_t absmax_2chunks(uint4 v, uint4 w) {
     u16x2_t m0 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu),
                                            __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu));
@@ -82,11 +62,6 @@ __device__ __forceinline__ uint32_t absmax_2chunks(uint4 v, uint4 w) {
     u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
                                           __builtin_elementwise_max(m2, m3));
     return (uint32_t)(m.x > m.y ? m.x : m.y);
-}
-
-// Value of the partner lane (lane ^ 1).
-__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false);
 }
 
 // ---------------------------------------------------------------- scale

@@ -6,14 +6,17 @@
 // caches addressed through block_table / cache_seqlens).
 //
 // Work decomposition
-//   8-bit: each span (one sequence's window) is a contiguous run of
-//     width * R elements; threads stream 8-element chunks with 128-bit
-//     fp16 accesses and 64-bit byte accesses.
-//   Q4/Q6: one wavefront per token row (row segment of up to 1024 elements)
-//     handles that row of K and of V; lane l holds chunks l and l + 64, so a
-//     32-element block is one DPP quad and a 1024-element row needs no loop.
-//     The physical row is resolved once per wave from scalar loads of
-//     cache_seqlens / block_table.
+//   Contiguous 8-bit (the page's fp16_to_fp8 / fp8_to_fp16): each span (one
+//     sequence's window) is a contiguous run of width * R elements; threads
+//     stream 8-element chunks with 128-bit fp16 and 64-bit byte accesses.
+//   K/V conversions (Q4/Q6/Q8, and the per-tensor formats incl. paged
+//     8-bit): one wavefront per unit = (token row, tensor, row segment).
+//     fp16 -> compact: lane l owns 16 consecutive elements of the segment
+//     (1024 elements), so a 32-element block is a lane pair.  compact ->
+//     fp16: lane l holds 8-element chunks l and l + 64 of the segment, so
+//     each 128-bit store of the wave is contiguous.  The physical row is
+//     resolved once per wave from scalar loads of cache_seqlens /
+//     block_table.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -65,6 +68,7 @@ __device__ __forceinline__ void st_nt(uint16_t* p, uint32_t v) { __builtin_nonte
 
 // ---------------------------------------------------------------- row map
 
+// Launch geometry, computed by the host launcher for each call.
 struct QGeom {
     int32_t n_units;   // rows * ntens * nseg
     int32_t nseg;      // row segments per row
@@ -77,7 +81,6 @@ struct QGeom {
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
     return (__umulhi(n, f.mul) + n) >> f.shift;
 }
-
 
 // How logical rows map to cache rows.
 enum RowMode {
@@ -119,7 +122,6 @@ __device__ __forceinline__ int64_t resolve_row(const QLaunch& a, const QGeom& g,
 // segment g).  Units are numbered with the segment fastest, then the tensor,
 // then the row, so neighbouring waves share the row's paging lookup and
 // touch neighbouring memory.  One wavefront converts one unit.
-
 
 struct UnitRef {
     int64_t row;       // physical row (0 for a padding or skipped unit)

@@ -10,7 +10,11 @@ The conventions each function follows are stated at the top of
 ``kvq_oracle.c``; the operations are the ones the page "Implementation:
 Turboderp org Exllamav2 Ext Cache" lists (Description / Signature / I/O
 Contract): fp16<->8-bit, fp16->Q4/Q6 with per-block fp16 scales for K and V,
-the inverse, contiguous and paged layouts, and the host prefix compare.
+the inverse, contiguous and paged layouts, and the host prefix compare.  It
+also covers the extensions built on them: block Q8 (the page's Usage section
+lists a Q8 cache class), a format per tensor (8-bit on paged caches, K and V
+at different widths), the full-prefix widen before attention, and the bytes
+per token of each format.
 """
 import ctypes
 import os

@@ -17,12 +17,16 @@
  *     stored offset-binary  u = q + 2^(b-1);
  *   - packing as one little-endian bit stream per token row: code j of the
  *     row occupies bits [b*j, b*j + b) (4-bit: 8 codes per uint32 word,
- *     6-bit: 16 codes per 12 bytes);
+ *     6-bit: 16 codes per 12 bytes, 8-bit: one code per byte);
  *   - dequantization x' = fp16_rne((float)q * (float)s16);
  *   - "FP8 (unsigned 8-bit)" = the high byte of the fp16 bit pattern (e5m2 by
  *     truncation toward zero); back: byte << 8;
  *   - count_match: number of leading equal elements of the two arrays within
- *     min(max_a, len_a, len_b), one element at a time.
+ *     min(max_a, len_a, len_b), one element at a time;
+ *   - extensions: b = 8 block codes (the page's Usage section lists a Q8
+ *     cache), a format per tensor (fp8 high byte or Q4/Q6/Q8 for K and for
+ *     V, contiguous or paged), the widen of every cached position
+ *     [0, cache_seqlens[b] + width) of each sequence, and bytes per token.
  * Every step is written out plainly, one element at a time; no blocking,
  * vectorisation or reordering beyond the definition.
  *
