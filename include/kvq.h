@@ -8,7 +8,10 @@
  * per-block fp16 scales, its inverse, over contiguous or paged caches, and a
  * host-side matching-prefix count.  Tensors become raw pointers plus one
  * shape descriptor; the page's implicit "current stream" becomes an explicit
- * HIP stream argument.
+ * HIP stream argument.  Beyond the page's five functions: 8-bit block codes
+ * (wbits 8), a format per tensor (paged 8-bit; K and V at different widths
+ * in one launch), the widen of every cached position before attention, and
+ * the bytes per token of each format.
  *
  * Conventions shared by every device call
  *   - All device pointers belong to the current HIP device and are owned by
@@ -26,6 +29,10 @@
  *     before any launch; on error nothing is enqueued.
  *   - batch_size == 0 or width == 0 validates the arguments and returns 0
  *     without launching.
+ *   - Size limits: a row holds at most 2^20 elements (heads * head_dim), a
+ *     call converts fewer than 2^30 row segments of 1024 elements
+ *     (batch_size * width * tensors * segments per row), and a paged table
+ *     spans block_table_cols * page_size < 2^31 positions.
  *
  * Layouts (row = one token: heads * head_dim elements, R below)
  *   fp16 cache     [dim0, dim1, heads, head_dim]            uint16 (fp16 bits)
@@ -70,9 +77,11 @@ extern "C" {
 #define KVQ_ERR_NULL     -1  /* a required pointer is NULL, or a K/V triple is partial */
 #define KVQ_ERR_WBITS    -2  /* wbits not 4, 6 or 8 (or an unknown KVQ_FMT_* format) */
 #define KVQ_ERR_SHAPE    -3  /* heads/head_dim/dims not positive, head_dim % 32 (Q) or
-                                heads*head_dim % 8 (8-bit) not 0, paged page_size != dim1 */
+                                heads*head_dim % 8 (8-bit) not 0, paged page_size != dim1,
+                                heads*head_dim > 2^20 */
 #define KVQ_ERR_RANGE    -4  /* negative size or offset, window past dim0/dim1,
-                                block_table_cols <= 0 in paged mode, elem_bytes not 4/8 */
+                                block_table_cols <= 0 in paged mode, elem_bytes not 4/8,
+                                a size limit above exceeded */
 #define KVQ_ERR_ALIGN    -5  /* a device base pointer is not 16-byte aligned (int32 tables: 4) */
 #define KVQ_ERR_OVERLAP  -6  /* an output buffer overlaps another buffer of the call */
 #define KVQ_ERR_HIP      -7  /* the HIP runtime rejected the launch */

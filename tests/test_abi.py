@@ -54,6 +54,24 @@ def test_only_declared_symbols_exported():
     assert exported == _declared_symbols()
 
 
+def test_c_consumer(tmp_path, lib):
+    """A C99 program including the public headers, linked against the
+    library, exercising the host-side entry points (no GPU call)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    exe = tmp_path / "c_abi_check"
+    libdir = os.path.dirname(kvq.library_path())
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_abi_check.c"),
+           "-L", libdir, "-lkvq", "-Wl,-rpath," + libdir, "-o", str(exe)]
+    subprocess.run(cmd, check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
+    assert "c abi ok" in out.stdout
+
+
 def test_strerror_and_version(lib):
     assert kvq.kvq_strerror(0) == "success"
     for c in range(-7, 0):
