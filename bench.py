@@ -459,6 +459,26 @@ def secondary_workloads(torch, kvq, synth, wl):
         nb = 2 * cw.batch_size * cw.width * q_row_bytes(wb)
         out[name] = {kk: {"us": round(vv * 1e6, 2), "GB/s": round(nb / vv / 1e9, 1)} for kk, vv in kt.items()}
         del k, v, kq, vq, ks, vs, ko, vo
+    # the Q6 contiguous shape (189 MB per launch) with 4 rotated buffer sets
+    # filled on the device (more than the 256 MB MALL between reuses)
+    cw = synth.q6_contig()
+    sets = []
+    for i in range(4):
+        k = synth.device_normal_f16(t, cw.shape, 7000 + 2 * i, std=0.5)
+        v = synth.device_normal_f16(t, cw.shape, 7001 + 2 * i, std=0.5)
+        cs, ss = kvq.code_shape(cw.shape, 6), kvq.scale_shape(cw.shape)
+        sets.append((k, v, t.empty(cs, dtype=t.uint8, device="cuda"), t.empty(cs, dtype=t.uint8, device="cuda"),
+                     t.empty(ss, dtype=t.float16, device="cuda"), t.empty(ss, dtype=t.float16, device="cuda"),
+                     t.empty_like(k), t.empty_like(v)))
+    a6 = (cw.batch_size, cw.offset, cw.width)
+    kt = time_kernels(t, [
+        ("quant", lambda d: kvq.kvq_fp16_to_q_kv(sets[d][0], sets[d][2], sets[d][4], sets[d][1], sets[d][3],
+                                                 sets[d][5], *a6, wbits=6), [0, 1, 2, 3]),
+        ("dequant", lambda d: kvq.kvq_q_to_fp16_kv(sets[d][2], sets[d][6], sets[d][4], sets[d][3], sets[d][7],
+                                                   sets[d][5], *a6, wbits=6), [0, 1, 2, 3])], 16)
+    nb = 2 * cw.batch_size * cw.width * q_row_bytes(6)
+    out["q6_contig_cold"] = {kk: {"us": round(vv * 1e6, 2), "GB/s": round(nb / vv / 1e9, 1)} for kk, vv in kt.items()}
+    del sets
     # large paged K-Q4 + V-Q6 (8 GiB per fp16 cache), 8 rotated draws:
     # two single-width launches per direction vs one per-tensor launch
     mw = synth.mix_paged(draws=8)
