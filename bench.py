@@ -48,7 +48,7 @@ def parse():
     p.add_argument("--steps", type=int, default=640)
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
-    p.add_argument("--streams", type=int, default=4,
+    p.add_argument("--streams", type=int, default=2,
                    help="independent step chains replayed concurrently (1 = strictly serial steps)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' kernel timings")
