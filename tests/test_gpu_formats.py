@@ -259,3 +259,85 @@ def test_prefix_paged_workload(kvq):
     byte_diff(gather_rows(ko, valid).view(np.uint16), want, "prefix workload")
     cand = np.setdiff1d(np.random.default_rng(4).integers(0, shape[0] * shape[1], size=512), valid)[:256]
     assert (gather_rows(ko, cand).view(np.uint8) == SENTINEL).all()
+
+
+# ---------------------------------------------------------------- randomized sweep
+def _random_case(rng):
+    """One small seeded configuration: shape, mode, formats, window, tables."""
+    heads, head_dim = int(rng.integers(1, 5)), 32 * int(rng.integers(1, 6))
+    mode = ("contig", "paged", "prefix")[int(rng.integers(0, 3))]
+    fk, fv = (int(f) for f in rng.choice(FMTS, 2))
+    present = ("kv", "k", "v")[int(rng.choice(3, p=[0.8, 0.1, 0.1]))] if mode != "prefix" else "kv"
+    c = {"mode": mode, "fk": fk, "fv": fv, "present": present}
+    if mode == "contig":
+        dim0, dim1 = int(rng.integers(1, 6)), int(rng.integers(1, 12))
+        c["batch"] = int(rng.integers(0, dim0 + 1))
+        c["offset"] = int(rng.integers(0, dim1 + 1))
+        c["width"] = int(rng.integers(0, dim1 - c["offset"] + 1))
+        c["ps"], c["sl"], c["bt"] = 0, None, None
+    else:
+        ps, B, cols = int(rng.integers(1, 10)), int(rng.integers(1, 5)), int(rng.integers(1, 5))
+        dim0, dim1 = B * cols + int(rng.integers(0, 6)), ps
+        bt = rng.permutation(dim0).astype(np.int32)[:B * cols].reshape(B, cols).copy()
+        bad = rng.random(bt.shape) < 0.1
+        bt[bad] = rng.choice(np.array([-1, -7, dim0, dim0 + 3], np.int32), size=int(bad.sum()))
+        c["sl"] = rng.integers(-3, cols * ps + 3, size=B).astype(np.int32)
+        c["bt"], c["batch"], c["ps"] = bt, B, ps
+        c["offset"] = int(rng.integers(0, 4)) if mode == "paged" else 0
+        c["width"] = int(rng.integers(0, 2 * ps + 3))
+        c["max_len"] = int(rng.integers(0, cols * ps + 3))
+    c["shape"] = (dim0, dim1, heads, head_dim)
+    mag = 10.0 ** rng.uniform(-6, 3)
+    c["k"] = np.clip(rng.standard_normal(c["shape"]) * mag, -6e4, 6e4).astype(np.float16)
+    c["v"] = np.clip(rng.standard_normal(c["shape"]) * mag * 0.1, -6e4, 6e4).astype(np.float16)
+    return c
+
+
+def test_randomized_configs(kvq):
+    """300 seeded small configurations (contiguous, paged with invalid table
+    entries and out-of-range positions, full prefix; every format pair;
+    single-tensor calls) against the oracle, every byte of every buffer."""
+    t = torch()
+    rng = np.random.default_rng(20261203)
+    for case in range(300):
+        c = _random_case(rng)
+        shape, fk, fv = c["shape"], c["fk"], c["fv"]
+        has_k, has_v = "k" in c["present"], "v" in c["present"]
+        what = "case %d %s %s fmts (%d,%d) %s" % (case, c["mode"], shape, fk, fv, c["present"])
+        sld = dev(c["sl"]) if c["sl"] is not None else None
+        btd = dev(c["bt"]) if c["bt"] is not None else None
+        okc, oks = _np_bufs(shape, fk)
+        ovc, ovs = _np_bufs(shape, fv)
+        oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+        ko, vo = sentinel(shape, t.float16), sentinel(shape, t.float16)
+        if c["mode"] == "prefix":
+            # compact caches of every row, then widen each sequence's prefix
+            oracle.fp16_to_kv(c["k"], okc, oks, fk, c["v"], ovc, ovs, fv, shape[0], 0, shape[1])
+            kvq.kvq_kv_to_fp16_prefix(dev(okc), ko, None if oks is None else dev(oks), fk,
+                                      dev(ovc), vo, None if ovs is None else dev(ovs), fv,
+                                      c["batch"], c["width"], c["max_len"], sld, btd)
+            oracle.kv_to_fp16_prefix(okc, oko, oks, fk, ovc, ovo, ovs, fv, c["batch"], c["width"],
+                                     c["max_len"], c["sl"], c["bt"])
+            byte_diff(host(ko), oko.view(np.uint16), what + " K")
+            byte_diff(host(vo), ovo.view(np.uint16), what + " V")
+            continue
+        kc, ks = _dev_bufs(shape, fk)
+        vc, vs = _dev_bufs(shape, fv)
+        kd, vd = dev(c["k"]), dev(c["v"])
+        a = (c["batch"], c["offset"], c["width"], c["ps"], sld, btd)
+        kvq.kvq_fp16_to_kv(kd if has_k else None, kc if has_k else None, ks if has_k else None, fk,
+                           vd if has_v else None, vc if has_v else None, vs if has_v else None, fv, *a)
+        kvq.kvq_kv_to_fp16(kc if has_k else None, ko if has_k else None, ks if has_k else None, fk,
+                           vc if has_v else None, vo if has_v else None, vs if has_v else None, fv, *a)
+        oa = (c["batch"], c["offset"], c["width"], c["ps"], c["sl"], c["bt"])
+        oracle.fp16_to_kv(c["k"] if has_k else None, okc if has_k else None, oks if has_k else None, fk,
+                          c["v"] if has_v else None, ovc if has_v else None, ovs if has_v else None, fv, *oa)
+        oracle.kv_to_fp16(okc if has_k else None, oko if has_k else None, oks if has_k else None, fk,
+                          ovc if has_v else None, ovo if has_v else None, ovs if has_v else None, fv, *oa)
+        # absent tensors keep their sentinels on both sides
+        _cmp(kc, okc, what + " K compact")
+        _cmp(vc, ovc, what + " V compact")
+        _cmp(ks, oks, what + " K scales")
+        _cmp(vs, ovs, what + " V scales")
+        byte_diff(host(ko), oko.view(np.uint16), what + " K fp16")
+        byte_diff(host(vo), ovo.view(np.uint16), what + " V fp16")
