@@ -1,0 +1,155 @@
+"""Out-of-bounds write checks: every device buffer of a call is carved out of
+a larger allocation with 256 sentinel bytes on both sides, and after the
+call the guard bytes must be unchanged.  The shapes exercise the guarded
+kernels (row segments shorter than a full wave, chunk tails), the 12-byte
+Q6 stores and the 8-bit chunk tails; windows and tables reach the first
+and last rows of each buffer.  Outputs are also compared with the oracle.
+(Operations: ExLlamaV2 cache page, Description / I/O Contract: outputs are
+written in place on the touched rows only.)
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import SENTINEL, byte_diff, host, need_lib, sentinel_np, torch
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 256
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    assert torch().cuda.is_available(), "GPU tests need a ROCm device"
+    return need_lib()
+
+
+class Guarded:
+    """A device tensor of `shape` / `dtype` inside a sentinel-filled block
+    with GUARD bytes before and after it."""
+
+    def __init__(self, shape, dtype, init=None):
+        t = torch()
+        n = int(np.prod(shape)) * t.empty((), dtype=dtype).element_size()
+        self.block = t.full((n + 2 * GUARD,), SENTINEL, dtype=t.uint8, device="cuda")
+        self.tensor = self.block[GUARD:GUARD + n].view(dtype).view(shape)
+        if init is not None:
+            src = t.from_numpy(np.ascontiguousarray(init).view(np.uint8).reshape(-1)).cuda()
+            self.block[GUARD:GUARD + n].copy_(src)
+
+    def check(self, what):
+        b = host(self.block)
+        bad = np.nonzero(np.concatenate([b[:GUARD], b[-GUARD:]]) != SENTINEL)[0]
+        assert bad.size == 0, "%s: %d guard bytes written" % (what, bad.size)
+
+
+def _cs(shape, fmt):
+    return tuple(shape) if fmt == 0 else (shape[0], shape[1], shape[2], shape[3] * fmt // 8)
+
+
+def _ss(shape):
+    return (shape[0], shape[1], shape[2], shape[3] // 32)
+
+
+SHAPES = [(2, 5, 3, 96), (1, 3, 5, 1376), (2, 2, 1, 32)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_guard_fp8_contig(kvq, shape):
+    t = torch()
+    rng = np.random.default_rng(shape[3])
+    x = rng.standard_normal(shape).astype(np.float16)
+    gi = Guarded(shape, t.float16, x)
+    g8 = Guarded(shape, t.uint8)
+    gb = Guarded(shape, t.float16)
+    batch, offset, width = shape[0], 1, shape[1] - 1            # reaches the last row
+    kvq.kvq_fp16_to_fp8(gi.tensor, g8.tensor, batch, offset, width)
+    kvq.kvq_fp8_to_fp16(g8.tensor, gb.tensor, batch, offset, width)
+    w8, wb = sentinel_np(shape, np.uint8), sentinel_np(shape, np.float16)
+    oracle.fp16_to_fp8(x, w8, batch, offset, width)
+    oracle.fp8_to_fp16(w8, wb, batch, offset, width)
+    byte_diff(host(g8.tensor), w8, "fp8")
+    byte_diff(host(gb.tensor), wb.view(np.uint16), "fp16")
+    for g, n in ((gi, "input"), (g8, "8-bit"), (gb, "fp16 out")):
+        g.check("fp8 %s %s" % (shape, n))
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("wbits", [4, 6, 8])
+def test_guard_q_contig(kvq, shape, wbits):
+    t = torch()
+    rng = np.random.default_rng(shape[3] + wbits)
+    k = rng.standard_normal(shape).astype(np.float16)
+    v = (rng.standard_normal(shape) * 0.1).astype(np.float16)
+    gk, gv = Guarded(shape, t.float16, k), Guarded(shape, t.float16, v)
+    gkq, gvq = Guarded(_cs(shape, wbits), t.uint8), Guarded(_cs(shape, wbits), t.uint8)
+    gks, gvs = Guarded(_ss(shape), t.float16), Guarded(_ss(shape), t.float16)
+    gko, gvo = Guarded(shape, t.float16), Guarded(shape, t.float16)
+    batch, offset, width = shape[0], 0, shape[1]                 # every row, first to last
+    kvq.kvq_fp16_to_q_kv(gk.tensor, gkq.tensor, gks.tensor, gv.tensor, gvq.tensor, gvs.tensor,
+                         batch, offset, width, wbits=wbits)
+    kvq.kvq_q_to_fp16_kv(gkq.tensor, gko.tensor, gks.tensor, gvq.tensor, gvo.tensor, gvs.tensor,
+                         batch, offset, width, wbits=wbits)
+    okq, ovq = sentinel_np(_cs(shape, wbits), np.uint8), sentinel_np(_cs(shape, wbits), np.uint8)
+    oks, ovs = sentinel_np(_ss(shape), np.float16), sentinel_np(_ss(shape), np.float16)
+    oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+    oracle.fp16_to_q_kv(k, okq, oks, v, ovq, ovs, batch, offset, width, 0, None, None, wbits)
+    oracle.q_to_fp16_kv(okq, oko, oks, ovq, ovo, ovs, batch, offset, width, 0, None, None, wbits)
+    byte_diff(host(gkq.tensor), okq, "K codes")
+    byte_diff(host(gvs.tensor), ovs.view(np.uint16), "V scales")
+    byte_diff(host(gko.tensor), oko.view(np.uint16), "K out")
+    byte_diff(host(gvo.tensor), ovo.view(np.uint16), "V out")
+    for g, n in ((gk, "K in"), (gv, "V in"), (gkq, "K codes"), (gvq, "V codes"), (gks, "K scales"),
+                 (gvs, "V scales"), (gko, "K out"), (gvo, "V out")):
+        g.check("Q%d %s %s" % (wbits, shape, n))
+
+
+@pytest.mark.parametrize("fmts", [(0, 6), (4, 8), (6, 0), (8, 4)])
+@pytest.mark.parametrize("head_dim", [96, 1376])
+def test_guard_per_tensor_paged_and_prefix(kvq, fmts, head_dim):
+    """Pages of 3 tokens; the tables hold the first and the last physical
+    page: the last row (page dim0 - 1, slot 2) is converted by the window
+    calls and row 0 by the prefix widen."""
+    t = torch()
+    fk, fv = fmts
+    rng = np.random.default_rng(head_dim + 10 * fk + fv)
+    num_pages, ps, B, cols = 7, 3, 2, 3
+    shape = (num_pages, ps, 2, head_dim)
+    k = rng.standard_normal(shape).astype(np.float16)
+    v = (rng.standard_normal(shape) * 3).astype(np.float16)
+    bt = np.array([[num_pages - 1, 2, 4], [0, 5, 1]], np.int32)
+    sl = np.array([0, 1], np.int32)
+    width = cols * ps - 1                                         # sequence 1 reaches its last slot
+    gsl, gbt = Guarded(sl.shape, t.int32, sl), Guarded(bt.shape, t.int32, bt)
+    gk, gv = Guarded(shape, t.float16, k), Guarded(shape, t.float16, v)
+    gkc, gvc = Guarded(_cs(shape, fk), t.uint8), Guarded(_cs(shape, fv), t.uint8)
+    gks = Guarded(_ss(shape), t.float16) if fk else None
+    gvs = Guarded(_ss(shape), t.float16) if fv else None
+    gko, gvo = Guarded(shape, t.float16), Guarded(shape, t.float16)
+    gpo, gpv = Guarded(shape, t.float16), Guarded(shape, t.float16)
+    ten = lambda g: None if g is None else g.tensor
+    a = (B, 0, width, ps, gsl.tensor, gbt.tensor)
+    kvq.kvq_fp16_to_kv(gk.tensor, gkc.tensor, ten(gks), fk, gv.tensor, gvc.tensor, ten(gvs), fv, *a)
+    kvq.kvq_kv_to_fp16(gkc.tensor, gko.tensor, ten(gks), fk, gvc.tensor, gvo.tensor, ten(gvs), fv, *a)
+    max_len = cols * ps
+    kvq.kvq_kv_to_fp16_prefix(gkc.tensor, gpo.tensor, ten(gks), fk, gvc.tensor, gpv.tensor, ten(gvs), fv,
+                              B, 2, max_len, gsl.tensor, gbt.tensor)
+    okc, ovc = sentinel_np(_cs(shape, fk), np.uint8), sentinel_np(_cs(shape, fv), np.uint8)
+    oks = sentinel_np(_ss(shape), np.float16) if fk else None
+    ovs = sentinel_np(_ss(shape), np.float16) if fv else None
+    oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+    opo, opv = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+    oracle.fp16_to_kv(k, okc, oks, fk, v, ovc, ovs, fv, B, 0, width, ps, sl, bt)
+    oracle.kv_to_fp16(okc, oko, oks, fk, ovc, ovo, ovs, fv, B, 0, width, ps, sl, bt)
+    oracle.kv_to_fp16_prefix(okc, opo, oks, fk, ovc, opv, ovs, fv, B, 2, max_len, sl, bt)
+    byte_diff(host(gkc.tensor), okc, "K compact")
+    byte_diff(host(gvc.tensor), ovc, "V compact")
+    byte_diff(host(gko.tensor), oko.view(np.uint16), "K out")
+    byte_diff(host(gvo.tensor), ovo.view(np.uint16), "V out")
+    byte_diff(host(gpo.tensor), opo.view(np.uint16), "K prefix")
+    byte_diff(host(gpv.tensor), opv.view(np.uint16), "V prefix")
+    for g, n in ((gsl, "cache_seqlens"), (gbt, "block_table"), (gk, "K in"), (gv, "V in"), (gkc, "K compact"),
+                 (gvc, "V compact"), (gks, "K scales"), (gvs, "V scales"), (gko, "K out"), (gvo, "V out"),
+                 (gpo, "K prefix"), (gpv, "V prefix")):
+        if g is not None:
+            g.check("per-tensor %s %s %s" % (fmts, head_dim, n))
