@@ -130,9 +130,9 @@ struct UnitRef {
     bool live;         // false: nothing to store
 };
 
-// Dead units (grid padding past n_units, skipped rows) still read row 0 of
-// their tensor (always in bounds) and only have their stores masked off, so
-// no branch splits a wave's load stream.
+// Dead units (grid padding past n_units, skipped rows) resolve to row 0 of
+// their tensor (always in bounds) with live == false; the kernels return
+// at once for them (a wave-uniform branch).
 template <int MODE>
 __device__ __forceinline__ UnitRef unit_ref(const QLaunch& a, const QGeom& g, int32_t u) {
     UnitRef r;
@@ -239,6 +239,7 @@ __device__ __forceinline__ void narrow_unit(const QLaunch& a, const UnitRef& ur,
 template <int WBITS, int MODE, bool GUARD>
 __global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, QGeom g) {
     const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
+    if (!ur.live) return;   // wave-uniform: skipped rows and grid padding do nothing
     quant_unit<WBITS, GUARD>(a, ur, threadIdx.x & 63);
 }
 
@@ -246,6 +247,7 @@ __global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, QGeom g) 
 template <int MODE, bool GUARD>
 __global__ __launch_bounds__(kThreads) void narrow_kv_kernel(QLaunch a, QGeom g) {
     const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
+    if (!ur.live) return;   // wave-uniform: skipped rows and grid padding do nothing
     const int lane = threadIdx.x & 63;
     switch (ur.tensor ? a.fmt_v : a.fmt_k) {
         case 4: quant_unit<4, GUARD>(a, ur, lane); break;
@@ -364,12 +366,14 @@ __device__ __forceinline__ void widen_unit(const QLaunch& a, const UnitRef& ur, 
 template <int WBITS, int MODE, int NCH, bool GUARD>
 __global__ __launch_bounds__(kThreads) void dequant_kv_kernel(QLaunch a, QGeom g) {
     const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
+    if (!ur.live) return;   // wave-uniform: skipped rows and grid padding do nothing
     dequant_unit<WBITS, NCH, GUARD>(a, ur, threadIdx.x & 63);
 }
 
 template <int MODE, int NCH, bool GUARD>
 __global__ __launch_bounds__(kThreads) void widen_kv_kernel(QLaunch a, QGeom g) {
     const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
+    if (!ur.live) return;   // wave-uniform: skipped rows and grid padding do nothing
     const int lane = threadIdx.x & 63;
     switch (ur.tensor ? a.fmt_v : a.fmt_k) {
         case 4: dequant_unit<4, NCH, GUARD>(a, ur, lane); break;
