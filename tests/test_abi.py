@@ -72,6 +72,24 @@ def test_c_consumer(tmp_path, lib):
     assert "c abi ok" in out.stdout
 
 
+def test_fastdiv_constants_on_host(tmp_path):
+    """The host-computed multiply-shift constants of the row split give
+    n / d exactly (integer division) for numerators below 2^31: every
+    divisor up to 2^16, 2^k - 1 / 2^k / 2^k + 1 up to 2^31 - 1 and 2000
+    random ones, at the edges of the first and last 64 multiples."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("no C++ compiler")
+    exe = tmp_path / "fastdiv_check"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-Wall", "-Werror",
+                    "-I", os.path.join(ROOT, "kv_cache_quantization_kvq_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "fastdiv_check.cpp"), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "fastdiv ok" in out.stdout
+
+
 def test_strerror_and_version(lib):
     assert kvq.kvq_strerror(0) == "success"
     for c in range(-7, 0):
