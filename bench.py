@@ -298,6 +298,9 @@ def main():
                 "kernel": ("quant_kv_kernel<4>" if dom == "quant" else "dequant_kv_kernel<4>"),
                 "bytes_per_launch": wl.bytes_per_launch,
                 "avg_us": {k: round(v * 1e6, 3) for k, v in kt.items()}}
+    # counter cross-check: HBM bytes the counters saw per launch over the same duration
+    roofline["counter_GBps"] = (round(roofline["traffic"] / kt[dom] / 1e9, 1)
+                                if roofline["traffic"] is not None else None)
     # the pair figure: algorithmic bytes of one quantize and one dequantize
     # launch over the sum of their kernel times (cold rows, serial launches)
     pair_s = kt["quant"] + kt["dequant"]
