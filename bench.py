@@ -308,17 +308,17 @@ def main():
                    "frac": round(2 * wl.bytes_per_launch / pair_s / 1e9 / HBM_PEAK_GBS, 4),
                    "elements_per_s": round(2 * wl.elems_per_launch / pair_s, 1)}
 
-    # parity of the timed data: outputs of every draw against the oracle on a sample
-    import oracle
-
     def rows_fn(t, rows):
         idx = torch.from_numpy(np.asarray(rows, np.int64)).cuda()
         x = t.view(t.shape[0] * t.shape[1], -1).index_select(0, idx)
         a = x.cpu().numpy()
         return a.view(np.uint16) if a.dtype == np.float16 else a
 
+    # the CPU-baseline leg: the oracle timed on the host, and its outputs
+    # checked against the device outputs of the timed draws
     cpu = cpu_detail = None
     if not args.no_cpu_baseline:
+        import oracle
         log("timing the CPU oracle on %d draws" % args.cpu_draws)
         cb = cpu_baseline(wl, oracle, rows_fn, args.cpu_draws)
         # the oracle's outputs against the device outputs of the same rows
