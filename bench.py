@@ -403,6 +403,30 @@ def secondary_workloads(torch, kvq, synth, wl):
     kt = time_kernels(t, [("quant", wl.quant, [0]), ("dequant", wl.dequant, [0])], 4 * DRAWS)
     out["paged_q4_hot"] = {k: {"us": round(v * 1e6, 2), "GB/s": round(wl.bytes_per_launch / v / 1e9, 1)}
                            for k, v in kt.items()}
+    # per-layer use: 8 layers' caches (1024 pages each) converted with one
+    # shared paging draw, as a decode step does layer after layer -- the
+    # tables stay hot, each layer's rows are cold (344 MB between reuses)
+    lsh = (1024, w.shape[1], w.shape[2], w.shape[3])
+    lrng = np.random.default_rng(9009)
+    lsl = t.from_numpy(lrng.integers(0, 7937, size=w.batch_size).astype(np.int32)).cuda()
+    lbt = t.from_numpy(lrng.permutation(1024).astype(np.int32).reshape(w.batch_size, -1)).cuda()
+    layers = []
+    for i in range(8):
+        layers.append((synth.device_normal_f16(t, lsh, 9100 + 2 * i), synth.device_normal_f16(t, lsh, 9101 + 2 * i),
+                       t.empty(kvq.code_shape(lsh, 4), dtype=t.uint8, device="cuda"),
+                       t.empty(kvq.code_shape(lsh, 4), dtype=t.uint8, device="cuda"),
+                       t.empty(kvq.scale_shape(lsh), dtype=t.float16, device="cuda"),
+                       t.empty(kvq.scale_shape(lsh), dtype=t.float16, device="cuda"),
+                       t.empty(lsh, dtype=t.float16, device="cuda"), t.empty(lsh, dtype=t.float16, device="cuda")))
+    la = (w.batch_size, 0, w.width, w.shape[1], lsl, lbt)
+    kt = time_kernels(t, [
+        ("quant", lambda i: kvq.kvq_fp16_to_q_kv(layers[i][0], layers[i][2], layers[i][4], layers[i][1],
+                                                 layers[i][3], layers[i][5], *la, 4), list(range(8))),
+        ("dequant", lambda i: kvq.kvq_q_to_fp16_kv(layers[i][2], layers[i][6], layers[i][4], layers[i][3],
+                                                   layers[i][7], layers[i][5], *la, 4), list(range(8)))], 16 * 8)
+    out["paged_q4_layers_shared_table"] = {k: {"us": round(v * 1e6, 2), "GB/s": round(wl.bytes_per_launch / v / 1e9, 1)}
+                                           for k, v in kt.items()}
+    del layers
     # other block widths on the paged workload
     for wb in (6, 8):
         other = PagedKV(torch, kvq, synth, wbits=wb, share=wl)
