@@ -27,7 +27,6 @@ namespace kvq {
 #endif
 constexpr int kWaves = KVQ_WAVES_PER_BLOCK;   // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kFp8Cpt = 4;                // chunks per thread, 8-bit kernels
 
 // ---------------------------------------------------------------- memory policy
 //
@@ -386,45 +385,48 @@ __global__ __launch_bounds__(kThreads) void widen_kv_kernel(QLaunch a, QGeom g) 
 // ---------------------------------------------------------------- 8-bit
 
 // Contiguous windows: each sequence's window is one run of width * R
-// elements, streamed 8 elements per chunk, kFp8Cpt chunks per thread.
+// elements, streamed 8 elements per chunk, CPT chunks per thread (4 for
+// large spans; 1 when that would leave the grid smaller than the chip).
+template <int CPT>
 __global__ __launch_bounds__(kThreads) void fp16_to_fp8_kernel(Fp8Launch a) {
     const int64_t cps = a.span_elems >> 3;
-    const int64_t c0 = (int64_t)blockIdx.x * (kThreads * kFp8Cpt) + threadIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.x * (kThreads * CPT) + threadIdx.x;
     for (int32_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
         const int64_t e0 = (int64_t)b * a.batch_stride_elems + a.first_elem;
         const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in) + e0);
         uint2* dst = reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.out) + e0);
-        uint4 v[kFp8Cpt];
+        uint4 v[CPT];
 #pragma unroll
-        for (int k = 0; k < kFp8Cpt; ++k) {
+        for (int k = 0; k < CPT; ++k) {
             const int64_t c = c0 + k * kThreads;
             v[k] = c < cps ? ld_nt(src + c) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int k = 0; k < kFp8Cpt; ++k) {
+        for (int k = 0; k < CPT; ++k) {
             const int64_t c = c0 + k * kThreads;
             if (c < cps) st_nt(dst + c, make_uint2(high_bytes(v[k].x, v[k].y), high_bytes(v[k].z, v[k].w)));
         }
     }
 }
 
+template <int CPT>
 __global__ __launch_bounds__(kThreads) void fp8_to_fp16_kernel(Fp8Launch a) {
     const int64_t cps = a.span_elems >> 3;
-    const int64_t c0 = (int64_t)blockIdx.x * (kThreads * kFp8Cpt) + threadIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.x * (kThreads * CPT) + threadIdx.x;
     for (int32_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
         const int64_t e0 = (int64_t)b * a.batch_stride_elems + a.first_elem;
         const uint2* src = reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.in) + e0);
         uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + e0);
-        uint2 v[kFp8Cpt];
+        uint2 v[CPT];
 #pragma unroll
-        for (int k = 0; k < kFp8Cpt; ++k) {
+        for (int k = 0; k < CPT; ++k) {
             const int64_t c = c0 + k * kThreads;
             v[k] = c < cps ? make_uint2(ld_nt(reinterpret_cast<const uint32_t*>(src + c)),
                                         ld_nt(reinterpret_cast<const uint32_t*>(src + c) + 1))
                            : make_uint2(0, 0);
         }
 #pragma unroll
-        for (int k = 0; k < kFp8Cpt; ++k) {
+        for (int k = 0; k < CPT; ++k) {
             const int64_t c = c0 + k * kThreads;
             if (c < cps)
                 st_nt(dst + c, make_uint4(widen_lo(v[k].x), widen_hi(v[k].x), widen_lo(v[k].y), widen_hi(v[k].y)));
@@ -477,9 +479,17 @@ static int launch(const void* fn, dim3 grid, dim3 block, void** args, void* stre
     return (int)hipLaunchKernel(fn, grid, block, args, 0, static_cast<hipStream_t>(stream));
 }
 
-static dim3 fp8_grid(const Fp8Launch& a) {
+// Chunks per thread: 4 unless the grid would then have fewer workgroups
+// than the chip has CUs (small windows), where 1 spreads the span wider.
+static int fp8_cpt(const Fp8Launch& a) {
     const int64_t cps = a.span_elems >> 3;
-    const int64_t gx = (cps + kThreads * kFp8Cpt - 1) / (kThreads * kFp8Cpt);
+    const int64_t blocks4 = (cps + kThreads * 4 - 1) / (kThreads * 4) * (int64_t)a.batch;
+    return blocks4 < 256 ? 1 : 4;
+}
+
+static dim3 fp8_grid(const Fp8Launch& a, int cpt) {
+    const int64_t cps = a.span_elems >> 3;
+    const int64_t gx = (cps + kThreads * cpt - 1) / (kThreads * cpt);
     const int32_t gy = a.batch < 65535 ? a.batch : 65535;
     return dim3((unsigned)gx, (unsigned)gy, 1);
 }
@@ -487,13 +497,19 @@ static dim3 fp8_grid(const Fp8Launch& a) {
 int launch_fp16_to_fp8(const Fp8Launch& a, void* stream) {
     Fp8Launch arg = a;
     void* args[] = {&arg};
-    return launch(reinterpret_cast<const void*>(&fp16_to_fp8_kernel), fp8_grid(a), dim3(kThreads), args, stream);
+    const int cpt = fp8_cpt(a);
+    const void* fn = cpt == 1 ? reinterpret_cast<const void*>(&fp16_to_fp8_kernel<1>)
+                              : reinterpret_cast<const void*>(&fp16_to_fp8_kernel<4>);
+    return launch(fn, fp8_grid(a, cpt), dim3(kThreads), args, stream);
 }
 
 int launch_fp8_to_fp16(const Fp8Launch& a, void* stream) {
     Fp8Launch arg = a;
     void* args[] = {&arg};
-    return launch(reinterpret_cast<const void*>(&fp8_to_fp16_kernel), fp8_grid(a), dim3(kThreads), args, stream);
+    const int cpt = fp8_cpt(a);
+    const void* fn = cpt == 1 ? reinterpret_cast<const void*>(&fp8_to_fp16_kernel<1>)
+                              : reinterpret_cast<const void*>(&fp8_to_fp16_kernel<4>);
+    return launch(fn, fp8_grid(a, cpt), dim3(kThreads), args, stream);
 }
 
 // Kernel variants.  fp16 -> compact: 64 lanes x 16 elements per segment,
