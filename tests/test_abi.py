@@ -242,6 +242,33 @@ def test_count_match_torch_inputs():
         kvq.kvq_count_match(a, b.to(torch.int32), 10)
 
 
+def test_binding_host_checks():
+    """The Python binding checks dtypes, devices and arguments before it calls
+    the library (host tensors are rejected: the library takes device
+    pointers)."""
+    import torch
+    shape = (2, 4, 2, 64)
+    f16 = torch.zeros(shape, dtype=torch.float16)
+    f32 = torch.zeros(shape, dtype=torch.float32)
+    codes = torch.zeros(kvq.code_shape(shape, 4), dtype=torch.uint8)
+    scales = torch.zeros(kvq.scale_shape(shape), dtype=torch.float16)
+    with pytest.raises(TypeError):
+        kvq.kvq_fp16_to_q_kv(f32, codes, scales, None, None, None, 1, 0, 2)
+    with pytest.raises(ValueError):
+        kvq.kvq_fp16_to_q_kv(f16, codes, scales, None, None, None, 1, 0, 2)      # host memory
+    with pytest.raises(TypeError):
+        kvq.kvq_fp16_to_fp8(f32, torch.zeros(shape, dtype=torch.uint8), 1, 0, 2)
+    with pytest.raises(ValueError):
+        kvq.kvq_fp16_to_kv(None, None, None, 4, None, None, None, 4, 1, 0, 2)     # neither K nor V
+    with pytest.raises(ValueError):
+        kvq.kvq_fp16_to_kv(f16, codes, scales, 5, None, None, None, 4, 1, 0, 2)   # unknown format
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_bytes_per_token(5, 8, 128)
+    assert e.value.code == WBITS
+    assert kvq.compact_shape(shape, kvq.KVQ_FMT_FP8) == shape
+    assert kvq.compact_shape(shape, kvq.KVQ_FMT_Q6) == (2, 4, 2, 48)
+
+
 # ---------------------------------------------------------------- per-tensor formats, prefix, capacity
 def kv(lib, to_compact=True, k=(A, A + GB, A + 2 * GB), fk=4, v=(A + 3 * GB, A + 4 * GB, A + 5 * GB), fv=4,
        s=None, batch=2, offset=0, width=4, page_size=0, sl=None, bt=None, cols=0):
