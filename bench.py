@@ -216,7 +216,7 @@ def oracle_detail(wl, oracle, rows_fn, kvq):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each token row "
+        print("bench.py measures one GPU: the library has no multi-GPU path (each token row "
               "converts independently; sharding by heads or sequences needs no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
