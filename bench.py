@@ -17,6 +17,9 @@ the steps (launch overhead off the host) between device synchronisations.
 Output: one JSON line (metric, value = algorithmic GB/s of the whole job,
 ms_per_step, roofline of the dominant kernel measured with HIP events,
 cpu_baseline = the CPU oracle on a bounded sample, timed on the host cores).
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
 """
 import argparse
 import hashlib
@@ -377,10 +380,16 @@ def traffic_for(kernel, algo_bytes):
 
 
 def sources_digest():
+    """sha256 of the kernel sources with comments and whitespace removed, so
+    that the recorded counters stay attached to the code they measured."""
+    import re
     h = hashlib.sha256()
     for f in ("kvq_kernels.hip", "kvq_device.h", "kvq_internal.h"):
-        with open(os.path.join(ROOT, "kv_cache_quantization_kvq_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "kv_cache_quantization_kvq_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

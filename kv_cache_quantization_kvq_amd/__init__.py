@@ -13,6 +13,9 @@ Operations (ExLlamaV2 cache page, Description / Signature / I/O Contract):
                                        scales, K and V in one launch,
                                        contiguous or paged
   kvq_count_match                      host matching-prefix length
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
 """
 import ctypes
 import os

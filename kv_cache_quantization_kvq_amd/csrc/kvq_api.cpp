@@ -5,6 +5,9 @@
 // (batch_size, offset, width, page_size, cache_seqlens, block_table, wbits;
 // dtype checks kHalf <-> kUInt8).  Validation happens entirely on the host,
 // before anything is enqueued.
+//
+// (The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+// Exllamav2 Ext Cache".)
 #include <stdint.h>
 #include <string.h>
 

@@ -12,6 +12,9 @@
 //   value  x' = fp16_rne(q * s16)
 // How each is computed here without a per-element IEEE divide is described
 // next to the function that does it.
+//
+// (The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+// Exllamav2 Ext Cache".)
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -17,6 +17,9 @@
 //     each 128-bit store of the wave is contiguous.  The physical row is
 //     resolved once per wave from scalar loads of cache_seqlens /
 //     block_table.
+//
+// (The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+// Exllamav2 Ext Cache".)
 #include "kvq_device.h"
 #include "kvq_internal.h"
 

@@ -21,6 +21,9 @@ block_table / cache_seqlens with page_size 256 in its example):
                 [0,65280]; width 256; K at 4 bits, V at 6 bits; token ids
                 int32 uniform in [0,2^17) of length 65536 with a planted first
                 mismatch
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
 """
 from dataclasses import dataclass, field
 from typing import Optional

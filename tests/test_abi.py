@@ -7,6 +7,9 @@ batch_size, offset, width, page_size (0 = contiguous), cache_seqlens,
 block_table, wbits in {4, 6}; count_match(a, b, max_a).
 Fake device addresses are used only in calls that must be rejected by the
 host validation (or do no work), so no kernel is ever launched here.
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
 """
 import ctypes
 import os

@@ -7,6 +7,9 @@ functions have no paging arguments (ExLlamaV2 cache page, Signature); these
 entry points give each tensor its own format (8-bit high byte, Q4, Q6, Q8),
 page the 8-bit format, and widen every cached position of each sequence
 before attention (Usage section: conversion during the attention forward).
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
 """
 import numpy as np
 import pytest

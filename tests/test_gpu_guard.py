@@ -6,6 +6,9 @@ Q6 stores and the 8-bit chunk tails; windows and tables reach the first
 and last rows of each buffer.  Outputs are also compared with the oracle.
 (Operations: ExLlamaV2 cache page, Description / I/O Contract: outputs are
 written in place on the touched rows only.)
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
 """
 import numpy as np
 import pytest

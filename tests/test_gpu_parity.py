@@ -11,6 +11,9 @@ Workloads are the seeded synthetic ones of kv_cache_quantization_kvq_amd.synth
 (fp8 [1,256,8,128]; Q4 [4,2048,8,128] window 1024+512 with outliers; Q6
 [8,4096,8,128] with zero tokens; paged Q4 4096 pages x 256; paged K-Q4/V-Q6
 16384 pages x 256) plus small ragged shapes and edge cases.
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
 """
 import numpy as np
 import pytest

@@ -4,6 +4,9 @@ routine), exact rational arithmetic, and the e5m2 format definition.
 
 The 8-bit format is the high byte of the fp16 pattern, "FP8 (unsigned 8-bit)"
 on the ExLlamaV2 cache page (Description of fp16_to_fp8 / fp8_to_fp16).
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
 """
 from fractions import Fraction
 

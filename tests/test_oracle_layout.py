@@ -7,6 +7,9 @@ updates", results written in place); paged mode when page_size > 0, with
 block_table mapping logical to physical pages and cache_seqlens giving each
 sequence's cache length; count_match returns the length of the matching
 prefix of two 1-D tensors, at most max_a.
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
 """
 import numpy as np
 import pytest

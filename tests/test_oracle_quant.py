@@ -7,6 +7,9 @@ wbits is 4 or 6) fixes the operation but not the numerics; the readings used
 round-half-to-even codes against the stored scale clamped to
 [-2^(b-1), 2^(b-1)-1], offset-binary storage, little-endian bit stream
 packing) are checked here against exact arithmetic and brute force.
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
 """
 import itertools
 from fractions import Fraction
