@@ -48,7 +48,7 @@ def q_row_bytes(wbits):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=640)
+    p.add_argument("--steps", type=int, default=6400)
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     p.add_argument("--streams", type=int, default=2,
