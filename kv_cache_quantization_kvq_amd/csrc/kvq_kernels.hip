@@ -293,6 +293,26 @@ __device__ __forceinline__ CodeChunk load_code_chunk(const uint8_t* __restrict__
     return q;
 }
 
+// The codes of chunk c only (the caller supplies q.s).
+template <int WBITS>
+__device__ __forceinline__ CodeChunk load_code_only(const uint8_t* __restrict__ codes_row, int32_t c) {
+    CodeChunk q;
+    if constexpr (WBITS == 4) {
+        q.lo = ld_nt(reinterpret_cast<const uint32_t*>(codes_row) + c);
+        q.hi = 0;
+    } else if constexpr (WBITS == 8) {
+        const uint32_t* g = reinterpret_cast<const uint32_t*>(codes_row) + 2 * c;
+        q.lo = ld_nt(g);
+        q.hi = ld_nt(g + 1);
+    } else {
+        const uint32_t* g = reinterpret_cast<const uint32_t*>(codes_row + 12 * (c >> 1) + 4 * (c & 1));
+        q.lo = ld_nt(g);
+        q.hi = ld_nt(g + 1);
+    }
+    q.s = 0;
+    return q;
+}
+
 template <int WBITS>
 __device__ __forceinline__ uint4 dequant_chunk(const CodeChunk& q, int32_t c) {
     const uint32_t s2 = q.s | (q.s << 16);
@@ -313,8 +333,13 @@ __device__ __forceinline__ uint4 dequant_chunk(const CodeChunk& q, int32_t c) {
     }
 }
 
-// Block dequantization of one unit.
-template <int WBITS, int NCH, bool GUARD>
+// Block dequantization of one unit.  SSCALE: fetch the segment's scales
+// with one scalar load instead of per-lane loads (whole segments only).
+// Measured within one build at the paged workload (43 MB per launch): the
+// single-width Q4 kernel -2% and Q8 -5%, Q6 unchanged, and the per-tensor
+// kernel (format switch) +6%; so only the single-width Q4 and Q8 kernels
+// enable it.
+template <int WBITS, int NCH, bool GUARD, bool SSCALE>
 __device__ __forceinline__ void dequant_unit(const QLaunch& a, const UnitRef& ur, int lane) {
     const int32_t R = a.R;
     const int32_t cpr = R >> 3;
@@ -323,11 +348,33 @@ __device__ __forceinline__ void dequant_unit(const QLaunch& a, const UnitRef& ur
     const uint16_t* scales = static_cast<const uint16_t*>(ur.tensor ? a.v_scales : a.k_scales) +
                              ur.row * (int64_t)(R >> 5);
     CodeChunk q[NCH];
+    if constexpr (GUARD || !SSCALE) {
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
-        if (GUARD) q[k] = c < cpr ? load_code_chunk<WBITS>(codes, scales, c) : CodeChunk{0, 0, 0};
-        else q[k] = load_code_chunk<WBITS>(codes, scales, c);
+        for (int k = 0; k < NCH; ++k) {
+            const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
+            if (GUARD) q[k] = c < cpr ? load_code_chunk<WBITS>(codes, scales, c) : CodeChunk{0, 0, 0};
+            else q[k] = load_code_chunk<WBITS>(codes, scales, c);
+        }
+    } else {
+        // Whole segment: its NCH * 16 scales are NCH * 8 dwords inside the
+        // row, 32-byte aligned (R is a multiple of 512 here), fetched with one
+        // scalar load; lane l picks the scale of its chunks k * 64 + l (block
+        // (k * 64 + l) / 4: dword k * 8 + l / 8, half (l / 4) & 1).
+        const uint32_t* sw = reinterpret_cast<const uint32_t*>(scales) + ur.seg * (NCH * 8);
+        uint32_t S[NCH * 8];
+#pragma unroll
+        for (int i = 0; i < NCH * 8; ++i) S[i] = __builtin_amdgcn_readfirstlane(sw[i]);
+        const int32_t di = lane >> 3;
+        const bool hi = (lane >> 2) & 1;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
+            q[k] = load_code_only<WBITS>(codes, c);
+            uint32_t w = S[k * 8];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) w = di == i ? S[k * 8 + i] : w;
+            q[k].s = hi ? (w >> 16) : (w & 0xFFFFu);
+        }
     }
     uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * R);
 #pragma unroll
@@ -369,7 +416,7 @@ template <int WBITS, int MODE, int NCH, bool GUARD>
 __global__ __launch_bounds__(kThreads) void dequant_kv_kernel(QLaunch a, QGeom g) {
     const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
     if (!ur.live) return;   // wave-uniform: skipped rows and grid padding do nothing
-    dequant_unit<WBITS, NCH, GUARD>(a, ur, threadIdx.x & 63);
+    dequant_unit<WBITS, NCH, GUARD, WBITS != 6>(a, ur, threadIdx.x & 63);
 }
 
 template <int MODE, int NCH, bool GUARD>
@@ -378,9 +425,9 @@ __global__ __launch_bounds__(kThreads) void widen_kv_kernel(QLaunch a, QGeom g) 
     if (!ur.live) return;   // wave-uniform: skipped rows and grid padding do nothing
     const int lane = threadIdx.x & 63;
     switch (ur.tensor ? a.fmt_v : a.fmt_k) {
-        case 4: dequant_unit<4, NCH, GUARD>(a, ur, lane); break;
-        case 6: dequant_unit<6, NCH, GUARD>(a, ur, lane); break;
-        case 8: dequant_unit<8, NCH, GUARD>(a, ur, lane); break;
+        case 4: dequant_unit<4, NCH, GUARD, false>(a, ur, lane); break;
+        case 6: dequant_unit<6, NCH, GUARD, false>(a, ur, lane); break;
+        case 8: dequant_unit<8, NCH, GUARD, false>(a, ur, lane); break;
         default: widen_unit<NCH, GUARD>(a, ur, lane); break;
     }
 }
