@@ -597,6 +597,7 @@ static const void* widen_fn(int nch, bool guard) {
 template <int W>
 static const void* single_fn(bool to_compact, int mode, int nch, bool guard) {
     if (to_compact) return mode == kPaged ? quant_fn<W, kPaged>(guard) : quant_fn<W, kContig>(guard);
+    if (mode == kPrefix) return dequant_fn<W, kPrefix>(nch, guard);
     return mode == kPaged ? dequant_fn<W, kPaged>(nch, guard) : dequant_fn<W, kContig>(nch, guard);
 }
 
@@ -632,10 +633,22 @@ static int launch_units(const QLaunch& a, bool to_compact, bool mixed, int mode,
     const dim3 grid((unsigned)((g.n_units + kWaves - 1) / kWaves));
     QLaunch arg = a;
     void* args[] = {&arg, &g};
+    // Per-tensor widening where every present tensor is Q4 (or every one
+    // Q8) runs the single-width kernel of that width: it has the scalar
+    // scale fetch, which the format-switch kernel does not take.
+    int wbits = a.wbits;
+    if (mixed && !to_compact) {
+        const int fk = a.k_src ? a.fmt_k : -1, fv = a.v_src ? a.fmt_v : -1;
+        const int f = fk < 0 ? fv : (fv < 0 || fv == fk ? fk : -1);
+        if (f == 4 || f == 8) {
+            mixed = false;
+            wbits = f;
+        }
+    }
     const void* fn;
     if (mixed) fn = mixed_fn(to_compact, mode, nch, guard);
-    else if (a.wbits == 4) fn = single_fn<4>(to_compact, mode, nch, guard);
-    else if (a.wbits == 6) fn = single_fn<6>(to_compact, mode, nch, guard);
+    else if (wbits == 4) fn = single_fn<4>(to_compact, mode, nch, guard);
+    else if (wbits == 6) fn = single_fn<6>(to_compact, mode, nch, guard);
     else fn = single_fn<8>(to_compact, mode, nch, guard);
     return launch(fn, grid, dim3(kThreads), args, stream);
 }

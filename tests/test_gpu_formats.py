@@ -205,7 +205,7 @@ def test_paged_fp8_workload(kvq):
 
 
 # ---------------------------------------------------------------- full prefix
-@pytest.mark.parametrize("fmts", [(4, 6), (8, 0), (0, 0), (6, 8)])
+@pytest.mark.parametrize("fmts", [(4, 6), (8, 0), (0, 0), (6, 8), (4, 4), (8, 8), (6, 6)])
 def test_prefix_small(kvq, fmts):
     """Every cached position of every sequence, with an invalid table entry,
     a cap (max_len) below some lengths, and width new tokens."""
