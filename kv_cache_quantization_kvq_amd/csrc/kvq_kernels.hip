@@ -172,7 +172,7 @@ __device__ __forceinline__ int32_t wave_index() {
 // masks the pieces past the row end of a partial last segment (pieces per
 // row are even, so a lane pair is in or out together).
 
-template <bool GUARD>
+// Pieces past the row end (in == false) read nothing and yield zeros.
 __device__ __forceinline__ void load_piece(const QLaunch& a, const UnitRef& ur, int32_t pc, bool in,
                                            uint4& x0, uint4& x1) {
     const uint4* src = reinterpret_cast<const uint4*>(
@@ -192,7 +192,7 @@ __device__ __forceinline__ void quant_unit(const QLaunch& a, const UnitRef& ur, 
     const int32_t pc = ur.seg * 64 + lane;
     const bool in = !GUARD || pc < (R >> 4);
     uint4 x0, x1;
-    load_piece<GUARD>(a, ur, pc, in, x0, x1);
+    load_piece(a, ur, pc, in, x0, x1);
     const uint32_t s16 = scale_from_absmax<WBITS>(pair_max(absmax_2chunks(x0, x1)));
     const ScaleOps so = prep_scale(s16);
     uint32_t u0[8], u1[8];
@@ -231,7 +231,7 @@ __device__ __forceinline__ void narrow_unit(const QLaunch& a, const UnitRef& ur,
     const int32_t pc = ur.seg * 64 + lane;
     const bool in = !GUARD || pc < (a.R >> 4);
     uint4 x0, x1;
-    load_piece<GUARD>(a, ur, pc, in, x0, x1);
+    load_piece(a, ur, pc, in, x0, x1);
     const uint4 d = make_uint4(high_bytes(x0.x, x0.y), high_bytes(x0.z, x0.w),
                                high_bytes(x1.x, x1.y), high_bytes(x1.z, x1.w));
     uint8_t* out = static_cast<uint8_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * (int64_t)a.R;
