@@ -369,10 +369,11 @@ def traffic_for(kernel, algo_bytes):
     if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(path):
-        if "=" in line and not line.startswith("#"):
-            k, v = line.split("=", 1)
-            kv[k.strip()] = v.strip()
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
     if kv.get("sources_sha256") != sources_digest():
         return None
     key = "%s_traffic_bytes_per_launch" % kernel

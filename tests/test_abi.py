@@ -36,7 +36,8 @@ def lib():
 def _declared_symbols():
     names = set()
     for h in ("kvq.h", "kvq_selftest.h"):
-        text = open(os.path.join(ROOT, "include", h)).read()
+        with open(os.path.join(ROOT, "include", h)) as fh:
+            text = fh.read()
         names |= set(re.findall(r"KVQ_API\s+[\w\s\*]+?\b(kvq_\w+)\s*\(", text))
     return names
 

@@ -130,12 +130,13 @@ def _read_golden_pack():
     import os
     path = os.path.join(os.path.dirname(__file__), "golden", "pack_vectors.txt")
     cases = []
-    for line in open(path):
-        line = line.strip()
-        if not line or line.startswith("#"):
-            continue
-        wb, codes, hexbytes = line.split("|")
-        cases.append((int(wb), [int(c) for c in codes.split()], bytes.fromhex(hexbytes.strip())))
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            wb, codes, hexbytes = line.split("|")
+            cases.append((int(wb), [int(c) for c in codes.split()], bytes.fromhex(hexbytes.strip())))
     return cases
 
 
@@ -190,7 +191,9 @@ def _round_trip_ok(x_bits, s16, u, xq_bits, wbits):
     q = u.astype(np.int64) - Z
     clamped = (q == -Z) | (q == Z - 1) & (np.abs(x) > (Z - 0.5) * s)
     ok = np.isinf(xq) | clamped
-    ulp = np.spacing(np.abs(xq).astype(np.float16)).astype(np.float64)
+    ulp = np.zeros_like(xq)
+    fin = np.isfinite(xq)                   # infinite x' is accepted above
+    ulp[fin] = np.spacing(np.abs(xq[fin]).astype(np.float16)).astype(np.float64)
     ok |= np.abs(x - xq) <= s / 2 + ulp / 2
     return ok.all()
 
