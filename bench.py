@@ -208,7 +208,17 @@ def oracle_detail(wl, oracle, rows_fn, kvq):
     if m_oracle != m_lib:
         log("count_match mismatch: oracle %d, library %d" % (m_oracle, m_lib))
         sys.exit(4)
-    return {"single_thread": {"GB/s": round(rows.size * q_row_bytes(4) * 2 / dt / 1e9, 4),
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": cpu_model, "host_threads_available": len(os.sched_getaffinity(0)),
+            "single_thread": {"GB/s": round(rows.size * q_row_bytes(4) * 2 / dt / 1e9, 4),
                               "elements_per_s": round(rows.size * ROW * 2 / dt, 1),
                               "sample": "%d K rows of one paged-Q4 step quantized then dequantized, 1 thread"
                                         % rows.size},
