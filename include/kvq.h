@@ -97,7 +97,7 @@ typedef struct kvq_shape {
 /*
  * fp16 -> 8-bit over the contiguous window: rows (b, offset + t) for
  * b < batch_size, t < width.  ExLlamaV2 cache page, Description of
- * fp16_to_fp8 ("FP16 cache tensors to FP8 (unsigned 8-bit)", strided 4D
+ * fp16_to_fp8 (fp16 cache tensors to the 8-bit format, unsigned bytes, strided 4D
  * layout with batch_size, offset, width for partial updates).
  *   in_f16  device, fp16 [dim0, dim1, heads, head_dim], read
  *   out_u8  device, uint8 of the same shape, written on the window only
@@ -109,8 +109,8 @@ KVQ_API int kvq_fp16_to_fp8(const void* in_f16, void* out_u8, kvq_shape s,
 
 /*
  * 8-bit -> fp16, the inverse of kvq_fp16_to_fp8 over the same window.
- * ExLlamaV2 cache page, Description of fp8_to_fp16 (same shape validation and
- * strided access pattern).
+ * ExLlamaV2 cache page, Description of fp8_to_fp16 (validated and laid out
+ * like the forward conversion).
  *   in_u8    device, uint8 [dim0, dim1, heads, head_dim], read
  *   out_f16  device, fp16 of the same shape, written on the window only
  */
@@ -151,7 +151,7 @@ KVQ_API int kvq_fp16_to_q_kv(const void* k_in, void* k_out, void* k_scales,
  * 4/6/8-bit codes + fp16 scales -> fp16 for K and V in one launch, over the
  * same rows as kvq_fp16_to_q_kv with the same arguments.  ExLlamaV2 cache
  * page, Description of q_to_fp16_kv (same paged/contiguous dual path) and
- * I/O Contract (writes dequantized FP16 values into k_out / v_out).
+ * I/O Contract (k_out / v_out receive the fp16 values).
  *   k_in, v_in          device, uint8 codes [dim0, dim1, heads, head_dim*wbits/8], read
  *   k_out, v_out        device, fp16 [dim0, dim1, heads, head_dim], written
  *   k_scales, v_scales  device, fp16 [dim0, dim1, heads, head_dim/32], read

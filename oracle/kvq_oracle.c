@@ -19,7 +19,7 @@
  *     row occupies bits [b*j, b*j + b) (4-bit: 8 codes per uint32 word,
  *     6-bit: 16 codes per 12 bytes, 8-bit: one code per byte);
  *   - dequantization x' = fp16_rne((float)q * (float)s16);
- *   - "FP8 (unsigned 8-bit)" = the high byte of the fp16 bit pattern (e5m2 by
+ *   - the page's unsigned 8-bit FP8 format = the high byte of the fp16 bit pattern (e5m2 by
  *     truncation toward zero); back: byte << 8;
  *   - count_match: number of leading equal elements of the two arrays within
  *     min(max_a, len_a, len_b), one element at a time;

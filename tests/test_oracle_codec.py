@@ -2,7 +2,7 @@
 not come from the oracle: numpy's IEEE binary16 conversion (a library
 routine), exact rational arithmetic, and the e5m2 format definition.
 
-The 8-bit format is the high byte of the fp16 pattern, "FP8 (unsigned 8-bit)"
+The 8-bit format is the high byte of the fp16 pattern (the page's FP8, stored unsigned)
 on the ExLlamaV2 cache page (Description of fp16_to_fp8 / fp8_to_fp16).
 
 (The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org

@@ -2,11 +2,11 @@
 
 The ExLlamaV2 cache page (Description, I/O Contract) fixes: contiguous
 [batch, seq, heads, head_dim] caches converted over positions
-[offset, offset + width) of each of batch_size sequences ("partial cache
-updates", results written in place); paged mode when page_size > 0, with
+[offset, offset + width) of each of batch_size sequences (a window of the
+cache, outputs updated in place); paged mode when page_size > 0, with
 block_table mapping logical to physical pages and cache_seqlens giving each
-sequence's cache length; count_match returns the length of the matching
-prefix of two 1-D tensors, at most max_a.
+sequence's cache length; count_match counts how many leading elements two
+1-D tensors share, up to max_a.
 
 (The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
 Exllamav2 Ext Cache".)

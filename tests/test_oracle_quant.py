@@ -1,7 +1,7 @@
 """Pins of the oracle's block quantization, dequantization and bit packing.
 
 The ExLlamaV2 cache page (Description of fp16_to_q_kv / q_to_fp16_kv; I/O
-Contract: k_scales / v_scales are "per-block quantization scale factors",
+Contract: k_scales / v_scales hold one scale factor per quantization block,
 wbits is 4 or 6) fixes the operation but not the numerics; the readings used
 (32-element blocks along head_dim, absmax / (2^(b-1)-1) in fp32 stored as fp16,
 round-half-to-even codes against the stored scale clamped to
