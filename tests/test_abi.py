@@ -246,6 +246,19 @@ def test_count_match_torch_inputs():
         kvq.kvq_count_match(a, b.to(torch.int32), 10)
 
 
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built HIP library every entry point raises: there is no
+    fallback path."""
+    monkeypatch.setattr(kvq, "_LIB", None)
+    monkeypatch.setattr(kvq._build, "LIB", "/nonexistent/libkvq.so")
+    with pytest.raises(RuntimeError):
+        kvq.load_library()
+    with pytest.raises(RuntimeError):
+        kvq.kvq_version()
+    with pytest.raises(RuntimeError):
+        kvq.kvq_count_match(np.arange(4, dtype=np.int32), np.arange(4, dtype=np.int32), 4)
+
+
 def test_binding_host_checks():
     """The Python binding checks dtypes, devices and arguments before it calls
     the library (host tensors are rejected: the library takes device
