@@ -193,6 +193,22 @@ def oracle_detail(wl, oracle, rows_fn, kvq):
     c, s = oracle.quant_rows(x, 4)
     oracle.dequant_rows(c, s, 4)
     dt = time.perf_counter() - t0
+    # the other formats on the same rows, one thread
+    per_format = {}
+    for wb in (6, 8):
+        t1 = time.perf_counter()
+        c6, s6 = oracle.quant_rows(x, wb)
+        oracle.dequant_rows(c6, s6, wb)
+        d6 = time.perf_counter() - t1
+        per_format["Q%d" % wb] = round(rows.size * q_row_bytes(wb) * 2 / d6 / 1e9, 4)
+    x4 = x.reshape(1, rows.size, HEADS, HEAD_DIM)
+    b8 = np.empty(x4.shape, np.uint8)
+    back = np.empty(x4.shape, np.float16)
+    t1 = time.perf_counter()
+    oracle.fp16_to_fp8(x4, b8, 1, 0, rows.size)
+    oracle.fp8_to_fp16(b8, back, 1, 0, rows.size)
+    d8 = time.perf_counter() - t1
+    per_format["8-bit"] = round(rows.size * ROW * 3 * 2 / d8 / 1e9, 4)
     from kv_cache_quantization_kvq_amd import synth
     mw = synth.mix_paged()
     a, b = mw.extra["ids_a"], mw.extra["ids_b"]
@@ -218,6 +234,7 @@ def oracle_detail(wl, oracle, rows_fn, kvq):
     except OSError:
         pass
     return {"cpu_model": cpu_model, "host_threads_available": len(os.sched_getaffinity(0)),
+            "single_thread_other_formats_GBps": per_format,
             "single_thread": {"GB/s": round(rows.size * q_row_bytes(4) * 2 / dt / 1e9, 4),
                               "elements_per_s": round(rows.size * ROW * 2 / dt, 1),
                               "sample": "%d K rows of one paged-Q4 step quantized then dequantized, 1 thread"
@@ -350,6 +367,14 @@ def main():
                          % (cb["rows"], args.cpu_draws, cb["threads"], cb["seconds"])}
 
     secondary = None if args.no_secondary else secondary_workloads(torch, kvq, synth, wl)
+    if secondary is not None:
+        def add_frac(d):
+            if isinstance(d, dict):
+                if "GB/s" in d:
+                    d["frac"] = round(d["GB/s"] / HBM_PEAK_GBS, 4)
+                for v in d.values():
+                    add_frac(v)
+        add_frac(secondary)
     if args.calibrate_copy:
         calibrate_copy(torch)
 
