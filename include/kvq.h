@@ -30,6 +30,7 @@
  *   - batch_size == 0 or width == 0 validates the arguments and returns 0
  *     without launching.
  *   - Size limits: a row holds at most 2^20 elements (heads * head_dim), a
+ *     cache at most 2^60 (dim0 * dim1 * heads * head_dim), a
  *     call converts fewer than 2^30 row segments of 1024 elements
  *     (batch_size * width * tensors * segments per row), and a paged table
  *     spans block_table_cols * page_size < 2^31 positions.

@@ -23,6 +23,13 @@ using kvq::Fp8Launch;
 using kvq::QLaunch;
 
 constexpr int64_t kMaxRowElems = 1 << 20;
+constexpr int64_t kMaxCacheElems = INT64_C(1) << 60;    // dim0 * dim1 * heads * head_dim
+
+// a * b for a, b >= 0, saturated at INT64_MAX (extents of the overlap check)
+int64_t sat_mul(int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -55,6 +62,7 @@ int check_shape(const kvq_shape& s, bool q_path) {
     const int64_t R = (int64_t)s.heads * s.head_dim;
     if (R > kMaxRowElems) return KVQ_ERR_SHAPE;
     if (q_path ? (s.head_dim % 32 != 0) : (R % 8 != 0)) return KVQ_ERR_SHAPE;
+    if ((int64_t)s.dim0 * s.dim1 > kMaxCacheElems / R) return KVQ_ERR_RANGE;
     return KVQ_OK;
 }
 
@@ -157,7 +165,7 @@ int kv_call(CallKind kind, bool to_compact, const void* k_src, void* k_dst, cons
         {v_src, to_compact ? f16b() : v_compact, false}, {v_dst, to_compact ? v_compact : f16b(), true},
         {v_scales, rows * scale_row_bytes(R, fmt_v), to_compact},
         {cache_seqlens, page_size ? (int64_t)batch_size * 4 : 0, false},
-        {block_table, page_size ? (int64_t)batch_size * block_table_cols * 4 : 0, false}};
+        {block_table, page_size ? sat_mul((int64_t)batch_size * block_table_cols, 4) : 0, false}};
     if (any_output_overlap(ext, 8)) return KVQ_ERR_OVERLAP;
     if (batch_size == 0 || per_seq == 0) return KVQ_OK;
 

@@ -165,6 +165,15 @@ def test_size_bounds(lib):
              quant=False) == RANGE
     f = lib.kvq_fp16_to_fp8
     assert f(A, A + GB, shp(d0=1, d1=2, h=8193, d=128), 0, 0, 2, None) == SHAPE
+    # a cache beyond 2^60 elements is RANGE, whatever the window
+    big = shp(d0=(1 << 31) - 1, d1=(1 << 31) - 1, h=8, d=128)
+    assert q(lib, s=big, batch=0) == RANGE
+    assert f(A, A + GB, big, 0, 0, 2, None) == RANGE
+    far = (1 << 60, 2 << 60, 3 << 60)                      # 2^50 elements: 2 PiB of fp16
+    assert q(lib, s=shp(d0=1 << 20, d1=1 << 20, h=8, d=128), k=far, v=(None,) * 3, batch=0) == 0
+    # extreme table extents of a call with nothing to do: no overflow, success
+    assert q(lib, s=shp(d0=4, d1=1), page_size=1, sl=A + 6 * GB, bt=A + 7 * GB, cols=(1 << 31) - 1,
+             batch=(1 << 31) - 1, width=0) == 0
 
 
 def test_q_zero_work_returns_ok(lib):
