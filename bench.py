@@ -448,6 +448,21 @@ def secondary_workloads(torch, kvq, synth, wl):
     kt = time_kernels(t, [("quant", wl.quant, [0]), ("dequant", wl.dequant, [0])], 4 * DRAWS)
     out["paged_q4_hot"] = {k: {"us": round(v * 1e6, 2), "GB/s": round(wl.bytes_per_launch / v / 1e9, 1)}
                            for k, v in kt.items()}
+    # the paged-Q4 step called eagerly from Python (no graph), one stream:
+    # host submission time per step beside the wall time per step
+    n_eager = 640
+    for i in range(64):
+        wl.step(i % DRAWS)
+    t.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_eager):
+        wl.step(i % DRAWS)
+    t1 = time.perf_counter()
+    t.cuda.synchronize()
+    t2 = time.perf_counter()
+    out["paged_q4_eager"] = {"steps": n_eager, "host_us_per_step": round((t1 - t0) / n_eager * 1e6, 2),
+                             "us_per_step": round((t2 - t0) / n_eager * 1e6, 2),
+                             "GB/s": round(wl.bytes_per_step * n_eager / (t2 - t0) / 1e9, 1)}
     # per-layer use: 8 layers' caches (1024 pages each) converted with one
     # shared paging draw, as a decode step does layer after layer -- the
     # tables stay hot, each layer's rows are cold (344 MB between reuses)

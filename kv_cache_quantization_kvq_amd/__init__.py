@@ -104,9 +104,26 @@ def kvq_version():
 
 
 # ---------------------------------------------------------------- marshalling helpers
+#
+# These run on every call, so they keep the per-call Python work small: the
+# torch module and the current-stream query are looked up once, devices are
+# compared by index, and the full diagnosis (which check failed) is only
+# made once a check has failed.
+
+_TORCH = None
+_RAW_STREAM = None
+_SHAPES = {}
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH, _RAW_STREAM
+    if _TORCH is None:
+        import torch
+        # the current stream's raw handle of a device index, without building
+        # a Stream object (the public query is the fallback)
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _TORCH = torch
+    return _TORCH
 
 
 def _check(rc, fn):
@@ -114,39 +131,54 @@ def _check(rc, fn):
         raise KvqError(rc, fn)
 
 
+def _shape_struct(shp):
+    st = _SHAPES.get(shp)
+    if st is None:
+        if len(_SHAPES) >= 256:
+            _SHAPES.clear()
+        st = _SHAPES[shp] = Shape(*shp)
+    return st
+
+
 def _dev_ptr(t, name, dtype, device=None):
-    torch = _torch()
+    """Device address of a contiguous tensor of `dtype` (None passes through);
+    `device` is a device index the tensor must be on, or None."""
     if t is None:
         return None
+    torch = _TORCH or _torch()
+    if (isinstance(t, torch.Tensor) and t.dtype is dtype and t.is_cuda and t.is_contiguous()
+            and (device is None or t.get_device() == device)):
+        return t.data_ptr()
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be a device tensor" % name)
-    if device is not None and t.device != device:
-        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
-    return t.data_ptr()
+    if device is not None and t.get_device() != device:
+        raise ValueError("%s is on %s, expected cuda:%d" % (name, t.device, device))
+    raise ValueError("%s must be contiguous" % name)
 
 
 def _table_ptr(t, name, device):
-    torch = _torch()
     if t is None:
         return None
-    return _dev_ptr(t, name, torch.int32, device)
+    return _dev_ptr(t, name, _torch().int32, device)
 
 
 def _stream_handle(stream, device):
-    torch = _torch()
+    """Raw HIP stream handle: `stream` (a torch stream or a handle), or the
+    current stream of device index `device`."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
+        torch = _TORCH or _torch()
+        if _RAW_STREAM is not None:
+            return _RAW_STREAM(device)
+        return torch.cuda.current_stream(device).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
 def _expect_shape(t, shape, name):
-    if t is not None and tuple(t.shape) != tuple(shape):
+    if t is not None and t.shape != shape:
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
 
@@ -163,7 +195,13 @@ def scale_shape(cache_shape):
 def _shape4(t, name):
     if t.dim() != 4:
         raise ValueError("%s must be 4-D [dim0, dim1, heads, head_dim]" % name)
-    return tuple(int(x) for x in t.shape)
+    return tuple(t.shape)
+
+
+def _device_of(t):
+    """Device index of a device tensor (-1 for host tensors, which the
+    pointer checks then reject)."""
+    return t.get_device()
 
 
 # ---------------------------------------------------------------- 8-bit
@@ -172,11 +210,11 @@ def kvq_fp16_to_fp8(in_tensor, out_tensor, batch_size, offset, width, stream=Non
     window, b < batch_size, t < width.  Asynchronous on `stream`."""
     torch = _torch()
     shp = _shape4(in_tensor, "in_tensor")
-    dev = in_tensor.device
     pi = _dev_ptr(in_tensor, "in_tensor", torch.float16)
+    dev = _device_of(in_tensor)
     po = _dev_ptr(out_tensor, "out_tensor", torch.uint8, dev)
     _expect_shape(out_tensor, shp, "out_tensor")
-    rc = load_library().kvq_fp16_to_fp8(pi, po, Shape(*shp), int(batch_size), int(offset),
+    rc = load_library().kvq_fp16_to_fp8(pi, po, _shape_struct(shp), int(batch_size), int(offset),
                                         int(width), _stream_handle(stream, dev))
     _check(rc, "kvq_fp16_to_fp8")
 
@@ -185,11 +223,11 @@ def kvq_fp8_to_fp16(in_tensor, out_tensor, batch_size, offset, width, stream=Non
     """uint8 cache -> fp16 cache (byte << 8) over the same window."""
     torch = _torch()
     shp = _shape4(in_tensor, "in_tensor")
-    dev = in_tensor.device
     pi = _dev_ptr(in_tensor, "in_tensor", torch.uint8)
+    dev = _device_of(in_tensor)
     po = _dev_ptr(out_tensor, "out_tensor", torch.float16, dev)
     _expect_shape(out_tensor, shp, "out_tensor")
-    rc = load_library().kvq_fp8_to_fp16(pi, po, Shape(*shp), int(batch_size), int(offset),
+    rc = load_library().kvq_fp8_to_fp16(pi, po, _shape_struct(shp), int(batch_size), int(offset),
                                         int(width), _stream_handle(stream, dev))
     _check(rc, "kvq_fp8_to_fp16")
 
@@ -205,7 +243,7 @@ def _q_common(quant, k_in, k_out, k_scales, v_in, v_out, v_scales, batch_size, o
     if ref is None:
         raise ValueError("%s: at least one of the K and V triples is required" % fname)
     shp = _shape4(ref, "cache")
-    dev = ref.device
+    dev = _device_of(ref)
     if wbits not in (4, 6, 8):
         raise ValueError("wbits must be 4, 6 or 8")
     cshape, sshape = code_shape(shp, wbits), scale_shape(shp)
@@ -231,7 +269,7 @@ def _q_common(quant, k_in, k_out, k_scales, v_in, v_out, v_scales, batch_size, o
         psl = _table_ptr(cache_seqlens, "cache_seqlens", dev)
         pbt = _table_ptr(block_table, "block_table", dev)
     fn = getattr(load_library(), fname)
-    rc = fn(*ptrs, Shape(*shp), int(batch_size), int(offset), int(width), int(page_size),
+    rc = fn(*ptrs, _shape_struct(shp), int(batch_size), int(offset), int(width), int(page_size),
             psl, pbt, cols, int(wbits), _stream_handle(stream, dev))
     _check(rc, fname)
 
@@ -271,7 +309,7 @@ def _kv_ptrs(to_compact, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fm
     if ref is None:
         raise ValueError("at least one of K and V is required")
     shp = _shape4(ref, "cache")
-    dev = ref.device
+    dev = _device_of(ref)
     ptrs = []
     for name, (src, dst, sc, fmt) in (("k", (k_in, k_out, k_scales, fmt_k)), ("v", (v_in, v_out, v_scales, fmt_v))):
         if src is None and dst is None:
@@ -312,7 +350,7 @@ def _per_tensor(fname, to_compact, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_
             raise ValueError("paged mode needs cache_seqlens and block_table")
         psl, pbt, cols = _tables(batch_size, cache_seqlens, block_table, dev)
     rc = getattr(load_library(), fname)(ptrs[0], ptrs[1], ptrs[2], int(fmt_k), ptrs[3], ptrs[4], ptrs[5],
-                                        int(fmt_v), Shape(*shp), int(batch_size), int(offset), int(width),
+                                        int(fmt_v), _shape_struct(shp), int(batch_size), int(offset), int(width),
                                         int(page_size), psl, pbt, cols, _stream_handle(stream, dev))
     _check(rc, fname)
 
@@ -340,7 +378,7 @@ def kvq_kv_to_fp16_prefix(k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, f
     ptrs, shp, dev = _kv_ptrs(False, k_in, k_out, k_scales, fmt_k, v_in, v_out, v_scales, fmt_v)
     psl, pbt, cols = _tables(batch_size, cache_seqlens, block_table, dev)
     rc = load_library().kvq_kv_to_fp16_prefix(ptrs[0], ptrs[1], ptrs[2], int(fmt_k), ptrs[3], ptrs[4],
-                                              ptrs[5], int(fmt_v), Shape(*shp), int(batch_size),
+                                              ptrs[5], int(fmt_v), _shape_struct(shp), int(batch_size),
                                               int(width), int(max_len), psl, pbt, cols,
                                               _stream_handle(stream, dev))
     _check(rc, "kvq_kv_to_fp16_prefix")
@@ -386,7 +424,7 @@ def kvq_selftest_codes(x_bits, s_bits, wbits, out, force_clamp=False, stream=Non
     16-bit tensors, out uint8 [ns, nx]).  force_clamp=False uses the kernels'
     own dispatch (defined for |x / s| < 2^(b-1) - 1/2 under normal scales)."""
     torch = _torch()
-    dev = x_bits.device
+    dev = _device_of(x_bits)
     px = _dev_ptr(x_bits.view(torch.int16), "x", torch.int16)
     ps = _dev_ptr(s_bits.view(torch.int16), "s", torch.int16, dev)
     po = _dev_ptr(out, "out", torch.uint8, dev)
@@ -398,7 +436,7 @@ def kvq_selftest_codes(x_bits, s_bits, wbits, out, force_clamp=False, stream=Non
 
 def kvq_selftest_scales(a_bits, wbits, out, stream=None):
     torch = _torch()
-    dev = a_bits.device
+    dev = _device_of(a_bits)
     pa = _dev_ptr(a_bits.view(torch.int16), "absmax", torch.int16)
     po = _dev_ptr(out.view(torch.int16), "out", torch.int16, dev)
     rc = load_library().kvq_selftest_scales(pa, a_bits.numel(), int(wbits), po,
@@ -410,7 +448,7 @@ def kvq_selftest_fastdiv(n, d, out, stream=None):
     """out[i] = n[i] // d through the kernels' multiply-shift divider (device
     int32 tensors, 0 <= n < 2^31, 1 <= d < 2^31)."""
     torch = _torch()
-    dev = n.device
+    dev = _device_of(n)
     pn = _dev_ptr(n, "n", torch.int32)
     po = _dev_ptr(out, "out", torch.int32, dev)
     _expect_shape(out, tuple(n.shape), "out")
