@@ -492,3 +492,71 @@ def test_graph_replay_matches_eager(kvq):
         t.cuda.synchronize()
         for o, r in zip(outs, ref):
             byte_diff(host(o), r, "graph replay %d" % rep)
+
+
+def test_paged_q4_concurrent_graph_chains(kvq):
+    """The paged Q4 workload (4096 pages x 256, batch 32, width 256) in the
+    benchmark's launch configuration: four paging draws captured in one HIP
+    graph as two concurrent chains (draw d on chain d % 2, quantize then
+    dequantize), replayed twice.  Every row touched by any draw is checked
+    against the oracle (a row shared by two draws is converted from the same
+    source, so the result does not depend on the order of the chains),
+    untouched rows are sampled against the sentinel, and the second replay
+    reproduces the first byte for byte."""
+    t = torch()
+    w = synth.q4_paged(draws=4)
+    shape = w.shape
+    _log("q4_paged concurrent chains %s, %d draws" % (shape, len(w.extra["tables"])))
+    k = synth.device_normal_f16(t, shape, w.extra["device_seed"])
+    v = synth.device_normal_f16(t, shape, w.extra["device_seed"] + 1)
+    kq, vq = sentinel(_cs(shape, 4), t.uint8), sentinel(_cs(shape, 4), t.uint8)
+    ks, vs = sentinel(_ss(shape), t.float16), sentinel(_ss(shape), t.float16)
+    ko, vo = sentinel(shape, t.float16), sentinel(shape, t.float16)
+    outs = (kq, ks, vq, vs, ko, vo)
+    tabs = [(dev(sl), dev(bt)) for sl, bt in w.extra["tables"]]
+
+    def step(d):
+        sl, bt = tabs[d]
+        kvq.kvq_fp16_to_q_kv(k, kq, ks, v, vq, vs, w.batch_size, w.offset, w.width, w.page_size, sl, bt, 4)
+        kvq.kvq_q_to_fp16_kv(kq, ko, ks, vq, vo, vs, w.batch_size, w.offset, w.width, w.page_size, sl, bt, 4)
+
+    chains = [t.cuda.Stream(), t.cuda.Stream()]
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        cap = t.cuda.current_stream()
+        for c in chains:
+            c.wait_stream(cap)
+        for d in range(len(tabs)):
+            with t.cuda.stream(chains[d % 2]):
+                step(d)
+        for c in chains:
+            cap.wait_stream(c)
+    t.cuda.synchronize()
+    g.replay()
+    t.cuda.synchronize()
+
+    touched = np.unique(np.concatenate([
+        r[r >= 0] for r in (oracle.call_rows(shape[0], shape[1], w.batch_size, w.offset, w.width,
+                                             w.page_size, sl, bt) for sl, bt in w.extra["tables"])]))
+    for name, src, q, s, o in (("K", k, kq, ks, ko), ("V", v, vq, vs, vo)):
+        c, sc = oracle.quant_rows(gather_rows(src, touched), 4)
+        byte_diff(gather_rows(q, touched), c, "chains %s codes" % name)
+        byte_diff(gather_rows(s, touched).view(np.uint16), sc, "chains %s scales" % name)
+        byte_diff(gather_rows(o, touched).view(np.uint16), oracle.dequant_rows(c, sc, 4),
+                  "chains %s dequant" % name)
+        rng = np.random.default_rng(11)
+        cand = np.setdiff1d(rng.integers(0, shape[0] * shape[1], size=512), touched)[:256]
+        assert cand.size > 0
+        assert (gather_rows(q, cand) == SENTINEL).all(), "chains %s untouched codes" % name
+        assert (gather_rows(s, cand).view(np.uint8) == SENTINEL).all(), "chains %s untouched scales" % name
+        assert (gather_rows(o, cand).view(np.uint8) == SENTINEL).all(), "chains %s untouched dequant" % name
+
+    first = [o.clone() for o in outs]
+    for o in outs:
+        o.view(t.uint8).fill_(SENTINEL)
+    t.cuda.synchronize()
+    g.replay()
+    t.cuda.synchronize()
+    for o, f, n in zip(outs, first, ("K codes", "K scales", "V codes", "V scales", "K out", "V out")):
+        assert t.equal(o.view(t.uint8), f.view(t.uint8)), "second replay differs: %s" % n
