@@ -521,9 +521,20 @@ def secondary_workloads(torch, kvq, synth, wl):
         sl, bt = wl.tables[d]
         kvq.kvq_kv_to_fp16_prefix(wl.kq, wl.ko, wl.ks, 4, wl.vq, wl.vo, wl.vs, 4, w.batch_size, w.width, max_len, sl, bt)
 
-    kt = time_kernels(t, [("prefix", prefix, list(range(DRAWS)))], 2 * DRAWS)
+    # the same launch with every sequence full (no position past its end)
+    full = t.full((w.batch_size,), max_len - w.width, dtype=t.int32, device="cuda")
+
+    def prefix_full(d):
+        kvq.kvq_kv_to_fp16_prefix(wl.kq, wl.ko, wl.ks, 4, wl.vq, wl.vo, wl.vs, 4, w.batch_size, w.width, max_len,
+                                  full, wl.tables[d][1])
+
+    kt = time_kernels(t, [("prefix", prefix, list(range(DRAWS))), ("full", prefix_full, list(range(DRAWS)))],
+                      2 * DRAWS)
     out["prefix_widen_q4_cold"] = {"us": round(kt["prefix"] * 1e6, 2), "MB": round(np.mean(pbytes) / 1e6, 1),
                                    "GB/s": round(np.mean(pbytes) / kt["prefix"] / 1e9, 1)}
+    fbytes = 2 * w.batch_size * max_len * q_row_bytes(4)
+    out["prefix_widen_q4_all_live_cold"] = {"us": round(kt["full"] * 1e6, 2), "MB": round(fbytes / 1e6, 1),
+                                            "GB/s": round(fbytes / kt["full"] / 1e9, 1)}
     # contiguous workloads (hot)
     x = t.from_numpy(synth.fp8_contig().k).cuda()
     o8 = t.empty(x.shape, dtype=t.uint8, device="cuda")
