@@ -35,12 +35,16 @@ _int = ctypes.c_int
 
 
 def lib():
-    """Load (building once if absent) the oracle shared library."""
+    """Load (building once if absent) the oracle shared library.  The
+    environment variable KVQ_ORACLE_LIB names another build of kvq_oracle.c
+    to load instead; the mutation test uses it to run the pins against
+    builds with planted mistakes."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("KVQ_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         sig = {
             "orc_f16_decode": (ctypes.c_double, [ctypes.c_uint16]),
             "orc_f16_encode_rne": (ctypes.c_uint16, [ctypes.c_double]),

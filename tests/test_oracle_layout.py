@@ -92,6 +92,15 @@ def test_contiguous_window_and_untouched(wbits):
     assert (ko[~inside].view(np.uint8) == 0xA5).all()
     want = oracle.dequant_rows(kq[inside].reshape(-1, H * cb), ks[inside].reshape(-1, H * D // 32), wbits)
     assert (ko[inside].reshape(-1, H * D).view(np.uint16) == want).all()
+    # K and V in one call: each tensor is dequantized with its own scales
+    # (the two tensors' scales differ: V is drawn independently of K)
+    assert not np.array_equal(ks[inside].view(np.uint16), vs[inside].view(np.uint16))
+    ko2, vo2 = _sentinel_like((B, S, H, D), np.float16), _sentinel_like((B, S, H, D), np.float16)
+    oracle.q_to_fp16_kv(kq, ko2, ks, vq, vo2, vs, batch, offset, width, 0, None, None, wbits)
+    for q, s, o in ((kq, ks, ko2), (vq, vs, vo2)):
+        assert (o[~inside].view(np.uint8) == 0xA5).all()
+        want = oracle.dequant_rows(q[inside].reshape(-1, H * cb), s[inside].reshape(-1, H * D // 32), wbits)
+        assert (o[inside].reshape(-1, H * D).view(np.uint16) == want).all()
 
 
 @pytest.mark.parametrize("wbits,page_size", [(4, 4), (6, 3), (4, 1)])
