@@ -201,6 +201,11 @@ def test_count_match_planted(dtype):
     assert oracle.count_match(a, a.copy(), n + 5) == n
     assert oracle.count_match(a, a[:10].copy(), n) == 10     # shorter b bounds it
     assert oracle.count_match(a, a.copy(), -3) == 0
+    # elements are compared whole: a difference in any one byte is a mismatch
+    for byte in range(np.dtype(dtype).itemsize):
+        b = a.copy()
+        b.view(np.uint8)[321 * b.itemsize + byte] ^= 0x40
+        assert oracle.count_match(a, b, n) == 321
 
 
 @pytest.mark.parametrize("dtype", [np.int32, np.int64])

@@ -35,6 +35,8 @@ MUTANTS = [
      [("float r = nearbyintf(v);", "float r = roundf(v);", 1)]),
     ("lower clamp bound 1 - Z instead of -Z",
      [("if (r < (float)(-Z)) r = (float)(-Z);", "if (r < (float)(1 - Z)) r = (float)(1 - Z);", 1)]),
+    ("upper clamp bound Z instead of Z - 1",
+     [("if (r > (float)(Z - 1)) r = (float)(Z - 1);", "if (r > (float)Z) r = (float)Z;", 1)]),
     ("zero scale stores code -Z instead of 0",
      [("            q = 0;\n", "            q = -Z;\n", 1)]),
     ("two's complement storage instead of offset binary",
@@ -63,6 +65,8 @@ MUTANTS = [
      [("return (uint8_t)(h >> 8); }", "return (uint8_t)(h >> 7); }", 1)]),
     ("8-bit widening fills the low byte with 0x80",
      [("return (uint16_t)((uint16_t)b << 8); }", "return (uint16_t)(((uint16_t)b << 8) | 0x80); }", 1)]),
+    ("8-bit windows ignore the offset",
+     [("int64_t row = (int64_t)b * dim1 + offset + t;", "int64_t row = (int64_t)b * dim1 + t;", 2)]),
     ("contiguous rows ignore the window offset",
      [("return (int64_t)b * dim1 + offset + t;", "return (int64_t)b * dim1 + t;", 1)]),
     ("paged positions ignore the offset",
@@ -77,6 +81,10 @@ MUTANTS = [
        1)]),
     ("full prefix ends at cache_seqlens without the new tokens",
      [("int64_t end = (int64_t)cache_seqlens[b] + width;", "int64_t end = (int64_t)cache_seqlens[b];", 2)]),
+    ("full prefix clipped one position short of max_len",
+     [("if (end > max_len) end = max_len;", "if (end > max_len) end = max_len - 1;", 2)]),
+    ("count_match compares only the first byte of each element",
+     [("(size_t)elem_bytes) != 0)", "(size_t)1) != 0)", 1)]),
     ("count_match returns one past the first mismatch",
      [("            return i;\n", "            return i + 1;\n", 1)]),
     ("count_match ignores max_a",
