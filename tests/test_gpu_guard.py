@@ -156,3 +156,70 @@ def test_guard_per_tensor_paged_and_prefix(kvq, fmts, head_dim):
                  (gpo, "K prefix"), (gpv, "V prefix")):
         if g is not None:
             g.check("per-tensor %s %s %s" % (fmts, head_dim, n))
+
+
+class Offset:
+    """A device tensor whose base address is `off` bytes past a 256-byte
+    boundary (16-byte aligned, as the library requires, but not 32- or
+    64-byte aligned for off = 16 or 48)."""
+
+    def __init__(self, shape, dtype, off, init=None):
+        t = torch()
+        n = int(np.prod(shape)) * t.empty((), dtype=dtype).element_size()
+        self.block = t.full((n + 512,), SENTINEL, dtype=t.uint8, device="cuda")
+        base = self.block.data_ptr() % 256
+        start = (256 - base) % 256 + off
+        self.tensor = self.block[start:start + n].view(dtype).view(shape)
+        assert self.tensor.data_ptr() % 256 == off
+        if init is not None:
+            src = t.from_numpy(np.ascontiguousarray(init).view(np.uint8).reshape(-1)).cuda()
+            self.block[start:start + n].copy_(src)
+
+
+@pytest.mark.parametrize("off", [16, 48])
+@pytest.mark.parametrize("wbits", [4, 6, 8])
+@pytest.mark.parametrize("paged", [False, True])
+def test_sixteen_byte_aligned_buffers(kvq, off, wbits, paged):
+    """Every buffer of a quantize + dequantize round trip 16 bytes past (or
+    48 bytes past) a 256-byte boundary: the scalar whole-segment scale fetch
+    of the Q4 / Q8 dequantize and every vector access must still read and
+    write exactly the oracle's bytes.  Rows of 1024 elements (whole segments)
+    and of 2048."""
+    t = torch()
+    for head_dim in (128, 256):
+        rng = np.random.default_rng(off + wbits + head_dim + (7 if paged else 0))
+        if paged:
+            num_pages, ps, B, cols = 9, 4, 3, 3
+            shape = (num_pages, ps, 8, head_dim)
+            bt = rng.permutation(num_pages).astype(np.int32)[:B * cols].reshape(B, cols)
+            sl = np.array([0, 3, 5], np.int32)
+            batch, offset, width = B, 0, 7
+            tabs = (ps, Offset(sl.shape, t.int32, off, sl).tensor, Offset(bt.shape, t.int32, off, bt).tensor)
+            ref_tabs = (ps, sl, bt)
+        else:
+            shape = (3, 10, 8, head_dim)
+            batch, offset, width = 2, 3, 6
+            tabs = (0, None, None)
+            ref_tabs = (0, None, None)
+        k = (rng.standard_normal(shape) * 2).astype(np.float16)
+        v = (rng.standard_normal(shape) * 0.5).astype(np.float16)
+        gk, gv = Offset(shape, t.float16, off, k), Offset(shape, t.float16, off, v)
+        gkq, gvq = Offset(_cs(shape, wbits), t.uint8, off), Offset(_cs(shape, wbits), t.uint8, off)
+        gks, gvs = Offset(_ss(shape), t.float16, off), Offset(_ss(shape), t.float16, off)
+        gko, gvo = Offset(shape, t.float16, off), Offset(shape, t.float16, off)
+        kvq.kvq_fp16_to_q_kv(gk.tensor, gkq.tensor, gks.tensor, gv.tensor, gvq.tensor, gvs.tensor,
+                             batch, offset, width, *tabs, wbits=wbits)
+        kvq.kvq_q_to_fp16_kv(gkq.tensor, gko.tensor, gks.tensor, gvq.tensor, gvo.tensor, gvs.tensor,
+                             batch, offset, width, *tabs, wbits=wbits)
+        okq, ovq = sentinel_np(_cs(shape, wbits), np.uint8), sentinel_np(_cs(shape, wbits), np.uint8)
+        oks, ovs = sentinel_np(_ss(shape), np.float16), sentinel_np(_ss(shape), np.float16)
+        oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+        oracle.fp16_to_q_kv(k, okq, oks, v, ovq, ovs, batch, offset, width, *ref_tabs, wbits)
+        oracle.q_to_fp16_kv(okq, oko, oks, ovq, ovo, ovs, batch, offset, width, *ref_tabs, wbits)
+        what = "off %d Q%d %s head_dim %d" % (off, wbits, "paged" if paged else "contiguous", head_dim)
+        byte_diff(host(gkq.tensor), okq, what + " K codes")
+        byte_diff(host(gvq.tensor), ovq, what + " V codes")
+        byte_diff(host(gks.tensor), oks.view(np.uint16), what + " K scales")
+        byte_diff(host(gvs.tensor), ovs.view(np.uint16), what + " V scales")
+        byte_diff(host(gko.tensor), oko.view(np.uint16), what + " K out")
+        byte_diff(host(gvo.tensor), ovo.view(np.uint16), what + " V out")
