@@ -223,3 +223,63 @@ def test_sixteen_byte_aligned_buffers(kvq, off, wbits, paged):
         byte_diff(host(gvs.tensor), ovs.view(np.uint16), what + " V scales")
         byte_diff(host(gko.tensor), oko.view(np.uint16), what + " K out")
         byte_diff(host(gvo.tensor), ovo.view(np.uint16), what + " V out")
+
+
+@pytest.mark.parametrize("off", [16, 48])
+@pytest.mark.parametrize("fmts", [(4, 4), (4, 0), (8, 6), (8, 8)])
+def test_sixteen_byte_aligned_per_tensor_and_prefix(kvq, off, fmts):
+    """Per-tensor paged round trip and full-prefix widen (the uniform Q4 and
+    Q8 pairs take the single-width kernels with the scalar scale fetch), and
+    the contiguous 8-bit pair, with every buffer 16-byte aligned only."""
+    t = torch()
+    fk, fv = fmts
+    rng = np.random.default_rng(off + 10 * fk + fv)
+    num_pages, ps, B, cols = 9, 4, 3, 3
+    shape = (num_pages, ps, 8, 128)
+    bt = rng.permutation(num_pages).astype(np.int32)[:B * cols].reshape(B, cols)
+    sl = np.array([1, 4, 2], np.int32)
+    width, max_len = 6, cols * ps
+    k = (rng.standard_normal(shape) * 2).astype(np.float16)
+    v = (rng.standard_normal(shape) * 0.5).astype(np.float16)
+    gsl, gbt = Offset(sl.shape, t.int32, off, sl).tensor, Offset(bt.shape, t.int32, off, bt).tensor
+    gk, gv = Offset(shape, t.float16, off, k).tensor, Offset(shape, t.float16, off, v).tensor
+    gkc, gvc = Offset(_cs(shape, fk), t.uint8, off).tensor, Offset(_cs(shape, fv), t.uint8, off).tensor
+    gks = Offset(_ss(shape), t.float16, off).tensor if fk else None
+    gvs = Offset(_ss(shape), t.float16, off).tensor if fv else None
+    gko, gvo = Offset(shape, t.float16, off).tensor, Offset(shape, t.float16, off).tensor
+    gpk, gpv = Offset(shape, t.float16, off).tensor, Offset(shape, t.float16, off).tensor
+    a = (B, 0, width, ps, gsl, gbt)
+    kvq.kvq_fp16_to_kv(gk, gkc, gks, fk, gv, gvc, gvs, fv, *a)
+    kvq.kvq_kv_to_fp16(gkc, gko, gks, fk, gvc, gvo, gvs, fv, *a)
+    kvq.kvq_kv_to_fp16_prefix(gkc, gpk, gks, fk, gvc, gpv, gvs, fv, B, width, max_len, gsl, gbt)
+    okc, ovc = sentinel_np(_cs(shape, fk), np.uint8), sentinel_np(_cs(shape, fv), np.uint8)
+    oks = sentinel_np(_ss(shape), np.float16) if fk else None
+    ovs = sentinel_np(_ss(shape), np.float16) if fv else None
+    oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+    opk, opv = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+    oracle.fp16_to_kv(k, okc, oks, fk, v, ovc, ovs, fv, B, 0, width, ps, sl, bt)
+    oracle.kv_to_fp16(okc, oko, oks, fk, ovc, ovo, ovs, fv, B, 0, width, ps, sl, bt)
+    oracle.kv_to_fp16_prefix(okc, opk, oks, fk, ovc, opv, ovs, fv, B, width, max_len, sl, bt)
+    what = "off %d formats %s" % (off, fmts)
+    byte_diff(host(gkc), okc, what + " K compact")
+    byte_diff(host(gvc), ovc, what + " V compact")
+    if fk:
+        byte_diff(host(gks), oks.view(np.uint16), what + " K scales")
+    if fv:
+        byte_diff(host(gvs), ovs.view(np.uint16), what + " V scales")
+    byte_diff(host(gko), oko.view(np.uint16), what + " K out")
+    byte_diff(host(gvo), ovo.view(np.uint16), what + " V out")
+    byte_diff(host(gpk), opk.view(np.uint16), what + " K prefix")
+    byte_diff(host(gpv), opv.view(np.uint16), what + " V prefix")
+    # contiguous 8-bit, window rows 1..5 of 2 sequences, on the same fp16 data
+    cshape = (3, 12, 8, 128)
+    x = (rng.standard_normal(cshape) * 3).astype(np.float16)
+    gx = Offset(cshape, t.float16, off, x).tensor
+    g8, gb = Offset(cshape, t.uint8, off).tensor, Offset(cshape, t.float16, off).tensor
+    kvq.kvq_fp16_to_fp8(gx, g8, 2, 1, 5)
+    kvq.kvq_fp8_to_fp16(g8, gb, 2, 1, 5)
+    w8, wb = sentinel_np(cshape, np.uint8), sentinel_np(cshape, np.float16)
+    oracle.fp16_to_fp8(x, w8, 2, 1, 5)
+    oracle.fp8_to_fp16(w8, wb, 2, 1, 5)
+    byte_diff(host(g8), w8, what + " 8-bit")
+    byte_diff(host(gb), wb.view(np.uint16), what + " 8-bit back")
