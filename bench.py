@@ -51,7 +51,9 @@ def parse():
     p.add_argument("--steps", type=int, default=6400)
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
-    p.add_argument("--streams", type=int, default=2,
+    p.add_argument("--graph-steps", type=int, default=20 * DRAWS,
+                   help="steps per captured graph (each replay forks and joins the chains)")
+    p.add_argument("--streams", type=int, default=3,
                    help="independent step chains replayed concurrently (1 = strictly serial steps)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' kernel timings")
@@ -267,9 +269,12 @@ def main():
         wl.step(i % DRAWS)
     torch.cuda.synchronize()
 
-    # graphs: steps spread round-robin over `--streams` independent chains
-    # (different steps touch different rows, so they need no ordering between
-    # them; within a step, dequantize follows its quantize on the same chain)
+    # graphs of `--graph-steps` steps spread round-robin over `--streams`
+    # independent chains.  Within a step, dequantize follows its quantize on
+    # the same chain.  Steps of different paging draws touch different rows;
+    # steps of one draw recur every DRAWS steps, and if two of them overlap on
+    # different chains they write identical bytes to the same rows, so no
+    # result depends on how the chains interleave.
     graphs = None
     if not args.no_graph:
         chains = [torch.cuda.Stream() for _ in range(args.streams)]
@@ -290,13 +295,14 @@ def main():
                     c.wait_stream(cap)                       # fork
                 for d in range(n):
                     with torch.cuda.stream(chains[d % args.streams]):
-                        wl.step(d)
+                        wl.step(d % DRAWS)
                 for c in chains:
                     cap.wait_stream(c)                       # join
             return g
 
-        rem = args.steps % DRAWS
-        graphs = (capture(DRAWS), capture(rem) if rem else None)
+        per = max(1, args.graph_steps)
+        rem = args.steps % per
+        graphs = (capture(per), capture(rem) if rem else None)
         graphs[0].replay()
         torch.cuda.synchronize()
 
@@ -305,7 +311,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if graphs:
-        for _ in range(args.steps // DRAWS):
+        for _ in range(args.steps // per):
             graphs[0].replay()
         if graphs[1] is not None:
             graphs[1].replay()
@@ -387,7 +393,7 @@ def main():
                       "heads": HEADS, "head_dim": HEAD_DIM, "batch": wl.w.batch_size,
                       "width": wl.w.width, "wbits": 4, "draws_rotated": DRAWS,
                       "bytes_per_step": wl.bytes_per_step,
-                      "timed": ("graph, %d chains" % args.streams) if graphs else "eager",
+                      "timed": ("graphs of %d steps, %d chains" % (per, args.streams)) if graphs else "eager",
                       "device": dev_name},
            "roofline": roofline, "kernel_pair": kernel_pair, "cpu_baseline": cpu}
     if cpu_detail is not None:

@@ -496,13 +496,14 @@ def test_graph_replay_matches_eager(kvq):
 
 def test_paged_q4_concurrent_graph_chains(kvq):
     """The paged Q4 workload (4096 pages x 256, batch 32, width 256) in the
-    benchmark's launch configuration: four paging draws captured in one HIP
-    graph as two concurrent chains (draw d on chain d % 2, quantize then
-    dequantize), replayed twice.  Every row touched by any draw is checked
-    against the oracle (a row shared by two draws is converted from the same
-    source, so the result does not depend on the order of the chains),
-    untouched rows are sampled against the sentinel, and the second replay
-    reproduces the first byte for byte."""
+    benchmark's launch configuration: eight steps over four paging draws
+    captured in one HIP graph as three concurrent chains (step i, draw i % 4,
+    on chain i % 3, quantize then dequantize), replayed twice.  Each draw
+    runs twice, on two different chains.  Every row touched by any draw is
+    checked against the oracle (a row converted by several steps is
+    converted from the same source, so the result does not depend on how the
+    chains interleave), untouched rows are sampled against the sentinel, and
+    the second replay reproduces the first byte for byte."""
     t = torch()
     w = synth.q4_paged(draws=4)
     shape = w.shape
@@ -520,16 +521,16 @@ def test_paged_q4_concurrent_graph_chains(kvq):
         kvq.kvq_fp16_to_q_kv(k, kq, ks, v, vq, vs, w.batch_size, w.offset, w.width, w.page_size, sl, bt, 4)
         kvq.kvq_q_to_fp16_kv(kq, ko, ks, vq, vo, vs, w.batch_size, w.offset, w.width, w.page_size, sl, bt, 4)
 
-    chains = [t.cuda.Stream(), t.cuda.Stream()]
+    chains = [t.cuda.Stream() for _ in range(3)]
     t.cuda.synchronize()
     g = t.cuda.CUDAGraph()
     with t.cuda.graph(g):
         cap = t.cuda.current_stream()
         for c in chains:
             c.wait_stream(cap)
-        for d in range(len(tabs)):
-            with t.cuda.stream(chains[d % 2]):
-                step(d)
+        for i in range(2 * len(tabs)):
+            with t.cuda.stream(chains[i % 3]):
+                step(i % len(tabs))
         for c in chains:
             cap.wait_stream(c)
     t.cuda.synchronize()
