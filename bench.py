@@ -300,7 +300,7 @@ def main():
                     cap.wait_stream(c)                       # join
             return g
 
-        per = max(1, args.graph_steps)
+        per = max(1, min(args.graph_steps, args.steps))
         rem = args.steps % per
         graphs = (capture(per), capture(rem) if rem else None)
         graphs[0].replay()
