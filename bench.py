@@ -252,6 +252,10 @@ def main():
               "converts independently; sharding by heads or sequences needs no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.streams < 1 or args.graph_steps < 1:
+        print("bench.py: --steps, --streams and --graph-steps must be at least 1, --warmup at least 0",
+              file=sys.stderr)
+        sys.exit(2)
     import torch
 
     import kv_cache_quantization_kvq_amd as kvq
