@@ -21,6 +21,11 @@
  *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
  *     the default stream).  A kernel fault surfaces at the caller's next
  *     synchronisation with that stream.
+ *   - A call enqueues exactly one kernel launch (none when it has nothing to
+ *     do) and no memory set, copy, allocation or synchronisation, so it may
+ *     be captured into a HIP graph; replays reread the tables' current
+ *     contents.  Calls that overlap in time (other streams, graph branches)
+ *     are safe when they write disjoint rows or identical bytes.
  *   - Every base pointer of a device buffer must be 16-byte aligned
  *     (allocations from hipMalloc or torch satisfy this); int32 tables need
  *     4-byte alignment.
