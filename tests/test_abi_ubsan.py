@@ -1,0 +1,46 @@
+"""The C ABI's host side (argument validation, extent and overlap
+arithmetic at extreme sizes, count_match) built with g++ and the
+undefined-behaviour sanitizer, aborting on the first report, and driven by
+the host-side ABI tests.  The kernel launchers are replaced by stand-ins
+that return an error (tests/host_launch_stub.cpp); no test reaches them."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# the host-side ABI tests that call into the library (not the ones that
+# inspect the built HIP library's file or compile other programs)
+HOST_TESTS = ("strerror_and_version or q_validation or selftest_fastdiv_validation or size_bounds or "
+              "zero_work or fp8_validation or count_match or binding_host_checks or per_tensor_validation or "
+              "prefix_validation or bytes_per_token")
+
+DRIVER = """
+import sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import kv_cache_quantization_kvq_amd as kvq
+kvq._build.LIB = {lib!r}
+kvq._LIB = None
+import pytest
+sys.exit(pytest.main(["-q", "-s", "-p", "no:cacheprovider", {test_file!r}, "-k", {tests_k!r}]))
+"""
+
+
+def test_host_abi_under_ubsan(tmp_path):
+    if shutil.which("g++") is None:
+        pytest.skip("no C++ compiler")
+    lib = str(tmp_path / "libkvq_host_ubsan.so")
+    csrc = os.path.join(ROOT, "kv_cache_quantization_kvq_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fvisibility=hidden",
+                    "-fsanitize=undefined", "-fno-sanitize-recover=all", "-Wall", "-Wextra",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(csrc, "kvq_api.cpp"),
+                    os.path.join(ROOT, "tests", "host_launch_stub.cpp"), "-o", lib], check=True)
+    driver = DRIVER.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=lib,
+                           test_file=os.path.join(ROOT, "tests", "test_abi.py"), tests_k=HOST_TESTS)
+    out = subprocess.run([sys.executable, "-c", driver], capture_output=True, text=True, timeout=300,
+                         env=dict(os.environ, UBSAN_OPTIONS="print_stacktrace=1"))
+    assert out.returncode == 0, "exit %d\n%s\n%s" % (out.returncode, out.stdout[-3000:], out.stderr[-3000:])
+    assert " passed" in out.stdout
