@@ -1,8 +1,9 @@
 """The C ABI's host side (argument validation, extent and overlap
-arithmetic at extreme sizes, count_match) built with g++ and the
-undefined-behaviour sanitizer, aborting on the first report, and driven by
-the host-side ABI tests.  The kernel launchers are replaced by stand-ins
-that return an error (tests/host_launch_stub.cpp); no test reaches them."""
+arithmetic at extreme sizes, count_match) built with g++ and the address and
+undefined-behaviour sanitizers, aborting on the first report, and driven by
+the host-side ABI tests in a Python process that preloads the address
+sanitizer's runtime.  The kernel launchers are replaced by stand-ins that
+return an error (tests/host_launch_stub.cpp); no test reaches them."""
 import os
 import shutil
 import subprocess
@@ -29,18 +30,22 @@ sys.exit(pytest.main(["-q", "-s", "-p", "no:cacheprovider", {test_file!r}, "-k",
 """
 
 
-def test_host_abi_under_ubsan(tmp_path):
+def test_host_abi_under_sanitizers(tmp_path):
     if shutil.which("g++") is None:
         pytest.skip("no C++ compiler")
-    lib = str(tmp_path / "libkvq_host_ubsan.so")
+    lib = str(tmp_path / "libkvq_host_sanitized.so")
+    asan_rt = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    if not os.path.isabs(asan_rt) or not os.path.exists(asan_rt):
+        pytest.skip("no address-sanitizer runtime")
     csrc = os.path.join(ROOT, "kv_cache_quantization_kvq_amd", "csrc")
     subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fvisibility=hidden",
-                    "-fsanitize=undefined", "-fno-sanitize-recover=all", "-Wall", "-Wextra",
+                    "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-Wall", "-Wextra",
                     "-I", os.path.join(ROOT, "include"), os.path.join(csrc, "kvq_api.cpp"),
                     os.path.join(ROOT, "tests", "host_launch_stub.cpp"), "-o", lib], check=True)
     driver = DRIVER.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=lib,
                            test_file=os.path.join(ROOT, "tests", "test_abi.py"), tests_k=HOST_TESTS)
     out = subprocess.run([sys.executable, "-c", driver], capture_output=True, text=True, timeout=300,
-                         env=dict(os.environ, UBSAN_OPTIONS="print_stacktrace=1"))
+                         env=dict(os.environ, LD_PRELOAD=asan_rt, ASAN_OPTIONS="detect_leaks=0",
+                                  UBSAN_OPTIONS="print_stacktrace=1"))
     assert out.returncode == 0, "exit %d\n%s\n%s" % (out.returncode, out.stdout[-3000:], out.stderr[-3000:])
     assert " passed" in out.stdout
