@@ -344,3 +344,69 @@ def test_randomized_configs(kvq):
         _cmp(vs, ovs, what + " V scales")
         byte_diff(host(ko), oko.view(np.uint16), what + " K fp16")
         byte_diff(host(vo), ovo.view(np.uint16), what + " V fp16")
+
+
+def test_every_entry_point_under_graph_capture(kvq):
+    """One call of each device entry point captured in a single HIP graph:
+    8-bit both ways, Q4 both ways, per-tensor (K Q6, V 8-bit) both ways and
+    the full-prefix widen.  Three replays, with the outputs refilled eagerly
+    and the device synchronised between them, each reproduce the eager
+    bytes."""
+    t = torch()
+    rng = np.random.default_rng(404)
+    num_pages, ps, B, cols = 12, 8, 3, 4
+    shape = (num_pages, ps, 4, 64)
+    k = dev((rng.standard_normal(shape) * 2).astype(np.float16))
+    v = dev((rng.standard_normal(shape) * 0.3).astype(np.float16))
+    bt = dev(rng.permutation(num_pages).astype(np.int32)[:B * cols].reshape(B, cols))
+    sl = dev(np.array([2, 9, 17], np.int32))
+    width, max_len = 10, cols * ps
+    cshape = (2, 16, 4, 64)
+    x = dev(rng.standard_normal(cshape).astype(np.float16))
+    outs = {
+        "x8": t.empty(cshape, dtype=t.uint8, device="cuda"),
+        "xb": t.empty(cshape, dtype=t.float16, device="cuda"),
+        "kq": t.empty(_cshape(shape, 4), dtype=t.uint8, device="cuda"),
+        "vq": t.empty(_cshape(shape, 4), dtype=t.uint8, device="cuda"),
+        "ks": t.empty(_sshape(shape), dtype=t.float16, device="cuda"),
+        "vs": t.empty(_sshape(shape), dtype=t.float16, device="cuda"),
+        "ko": t.empty(shape, dtype=t.float16, device="cuda"),
+        "vo": t.empty(shape, dtype=t.float16, device="cuda"),
+        "kc": t.empty(_cshape(shape, 6), dtype=t.uint8, device="cuda"),
+        "vc": t.empty(shape, dtype=t.uint8, device="cuda"),
+        "kcs": t.empty(_sshape(shape), dtype=t.float16, device="cuda"),
+        "kw": t.empty(shape, dtype=t.float16, device="cuda"),
+        "vw": t.empty(shape, dtype=t.float16, device="cuda"),
+        "kp": t.empty(shape, dtype=t.float16, device="cuda"),
+        "vp": t.empty(shape, dtype=t.float16, device="cuda"),
+    }
+    o = outs
+
+    def calls():
+        kvq.kvq_fp16_to_fp8(x, o["x8"], 2, 3, 9)
+        kvq.kvq_fp8_to_fp16(o["x8"], o["xb"], 2, 3, 9)
+        kvq.kvq_fp16_to_q_kv(k, o["kq"], o["ks"], v, o["vq"], o["vs"], B, 0, width, ps, sl, bt, 4)
+        kvq.kvq_q_to_fp16_kv(o["kq"], o["ko"], o["ks"], o["vq"], o["vo"], o["vs"], B, 0, width, ps, sl, bt, 4)
+        kvq.kvq_fp16_to_kv(k, o["kc"], o["kcs"], 6, v, o["vc"], None, 0, B, 0, width, ps, sl, bt)
+        kvq.kvq_kv_to_fp16(o["kc"], o["kw"], o["kcs"], 6, o["vc"], o["vw"], None, 0, B, 0, width, ps, sl, bt)
+        kvq.kvq_kv_to_fp16_prefix(o["kq"], o["kp"], o["ks"], 4, o["vq"], o["vp"], o["vs"], 4, B, width,
+                                  max_len, sl, bt)
+
+    def refill():
+        for tns in outs.values():
+            tns.view(t.uint8).fill_(SENTINEL)
+
+    refill()
+    calls()
+    ref = {name: host(tns).copy() for name, tns in outs.items()}
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        refill()
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        for name, tns in outs.items():
+            byte_diff(host(tns), ref[name], "graph replay %d: %s" % (rep, name))
