@@ -586,6 +586,16 @@ def secondary_workloads(torch, kvq, synth, wl):
                                                    sets[d][5], *a6, wbits=6), [0, 1, 2, 3])], 16)
     nb = 2 * cw.batch_size * cw.width * q_row_bytes(6)
     out["q6_contig_cold"] = {kk: {"us": round(vv * 1e6, 2), "GB/s": round(nb / vv / 1e9, 1)} for kk, vv in kt.items()}
+    # contiguous 8-bit at the same shape: each set's K cache narrowed into
+    # bytes and widened back (101 MB per launch), sets rotated
+    b8 = [t.empty(cw.shape, dtype=t.uint8, device="cuda") for _ in range(4)]
+    kt = time_kernels(t, [
+        ("to_8bit", lambda d: kvq.kvq_fp16_to_fp8(sets[d][0], b8[d], *a6), [0, 1, 2, 3]),
+        ("to_fp16", lambda d: kvq.kvq_fp8_to_fp16(b8[d], sets[d][6], *a6), [0, 1, 2, 3])], 16)
+    nb = cw.batch_size * cw.width * ROW * 3
+    out["fp8_contig_large_cold"] = {kk: {"us": round(vv * 1e6, 2), "GB/s": round(nb / vv / 1e9, 1)}
+                                    for kk, vv in kt.items()}
+    del b8
     del sets
     # large paged K-Q4 + V-Q6 (8 GiB per fp16 cache), 8 rotated draws:
     # two single-width launches per direction vs one per-tensor launch
