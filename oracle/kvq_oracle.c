@@ -30,6 +30,9 @@
  * Every step is written out plainly, one element at a time; no blocking,
  * vectorisation or reordering beyond the definition.
  *
+ * Below, "[Cache]" stands for that page; each function names the section
+ * (and, where the page is silent, the reading above) it follows.
+ *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fPIC -shared (IEEE-754
  * binary32 arithmetic through SSE, round-to-nearest-even, no FTZ/DAZ).
  *
@@ -47,7 +50,9 @@
 /* IEEE-754 binary16, from the format definition.                            */
 /* ------------------------------------------------------------------------ */
 
-/* Exact value of an fp16 bit pattern (every fp16 value is exact in double). */
+/* Exact value of an fp16 bit pattern (every fp16 value is exact in double).
+ * IEEE-754 binary16 definition; [Cache] I/O Contract names the fp16 (kHalf)
+ * caches this decodes. */
 double orc_f16_decode(uint16_t h)
 {
     int sign = (h >> 15) & 1;
@@ -76,7 +81,9 @@ static double round_half_even_nonneg(double n)
 }
 
 /* Correctly rounded (round-half-to-even) conversion of a double to fp16,
- * with gradual underflow and overflow to infinity. */
+ * with gradual underflow and overflow to infinity.  IEEE-754 binary16
+ * rounding; the reading of [Cache] stores scales and dequantized values as
+ * fp16 under this rounding. */
 uint16_t orc_f16_encode_rne(double v)
 {
     if (isnan(v)) return 0x7E00;
@@ -106,6 +113,8 @@ uint16_t orc_f16_encode_rne(double v)
 /* 8-bit format: the high byte of the fp16 pattern.                          */
 /* ------------------------------------------------------------------------ */
 
+/* [Cache] Description of fp16_to_fp8 / fp8_to_fp16 and I/O Contract (the
+ * unsigned 8-bit cache), read as the high byte of the fp16 pattern. */
 uint8_t orc_fp8_from_f16(uint16_t h) { return (uint8_t)(h >> 8); }
 uint16_t orc_f16_from_fp8(uint8_t b) { return (uint16_t)((uint16_t)b << 8); }
 
@@ -116,7 +125,9 @@ uint16_t orc_f16_from_fp8(uint8_t b) { return (uint16_t)((uint16_t)b << 8); }
 static int qmax_of(int wbits) { return (1 << (wbits - 1)) - 1; }   /* Q */
 static int zero_of(int wbits) { return 1 << (wbits - 1); }         /* Z */
 
-/* Scale of a block from its absmax a (an fp16 pattern, a >= 0):
+/* [Cache] Description of fp16_to_q_kv and I/O Contract (per-block scale
+ * factors), with the scale reading above.
+ * Scale of a block from its absmax a (an fp16 pattern, a >= 0):
  * s32 = a / Q in fp32, stored as fp16 round-half-even. */
 uint16_t orc_scale_from_absmax(uint16_t a_bits, int wbits)
 {
@@ -125,7 +136,9 @@ uint16_t orc_scale_from_absmax(uint16_t a_bits, int wbits)
     return orc_f16_encode_rne((double)s32);
 }
 
-/* Offset-binary codes of n elements under a given stored scale. */
+/* Offset-binary codes of n elements under a given stored scale.  [Cache]
+ * Description of fp16_to_q_kv (wbits-bit codes), with the code reading
+ * above. */
 void orc_quant_elems(const uint16_t* x, int64_t n, uint16_t s16, int wbits, uint8_t* u)
 {
     const int Z = zero_of(wbits);
@@ -146,7 +159,8 @@ void orc_quant_elems(const uint16_t* x, int64_t n, uint16_t s16, int wbits, uint
     }
 }
 
-/* One block of L elements: absmax -> scale -> codes. */
+/* One block of L elements: absmax -> scale -> codes ([Cache] Description of
+ * fp16_to_q_kv: block quantization). */
 void orc_quant_block(const uint16_t* x, int L, int wbits, uint16_t* s16_out, uint8_t* u_out)
 {
     /* absmax; -0 counts as 0.  The maximum of |x| is taken on the values. */
@@ -164,7 +178,8 @@ void orc_quant_block(const uint16_t* x, int L, int wbits, uint16_t* s16_out, uin
     orc_quant_elems(x, L, s16, wbits, u_out);
 }
 
-/* Dequantize n offset-binary codes with one stored scale. */
+/* Dequantize n offset-binary codes with one stored scale ([Cache]
+ * Description of q_to_fp16_kv, with the dequantization reading above). */
 void orc_dequant_elems(const uint8_t* u, int64_t n, uint16_t s16, int wbits, uint16_t* out)
 {
     const int Z = zero_of(wbits);
@@ -178,6 +193,8 @@ void orc_dequant_elems(const uint8_t* u, int64_t n, uint16_t s16, int wbits, uin
 
 /* ------------------------------------------------------------------------ */
 /* Packing: one little-endian bit stream; code j at bits [b*j, b*j + b).      */
+/* ([Cache] I/O Contract: packed wbits-bit codes; the bit order is the       */
+/* reading above.)                                                           */
 /* ------------------------------------------------------------------------ */
 
 void orc_pack_bits(const uint8_t* u, int64_t n, int wbits, uint8_t* out)
@@ -265,6 +282,9 @@ void orc_dequant_rows(const uint8_t* codes, const uint16_t* scales, int64_t n_ro
 /* (p < 0, page index past the table, or page outside [0, dim0)).             */
 /* ------------------------------------------------------------------------ */
 
+/* [Cache] Description (contiguous windows and the paged layout addressed
+ * through block_table / cache_seqlens) and Signature (batch_size, offset,
+ * width, page_size). */
 int64_t orc_resolve_row(int b, int t, int dim0, int dim1, int offset, int page_size,
                         const int32_t* cache_seqlens, const int32_t* block_table,
                         int bt_cols)
@@ -299,6 +319,7 @@ int64_t orc_call_rows(int dim0, int dim1, int batch_size, int offset, int width,
 /* Host buffers; a NULL K or V triple skips that half.                        */
 /* ------------------------------------------------------------------------ */
 
+/* [Cache] Description / Signature of fp16_to_q_kv: K and V together. */
 void orc_fp16_to_q_kv(const uint16_t* k_in, uint8_t* k_out, uint16_t* k_scales,
                       const uint16_t* v_in, uint8_t* v_out, uint16_t* v_scales,
                       int dim0, int dim1, int heads, int head_dim,
@@ -321,6 +342,8 @@ void orc_fp16_to_q_kv(const uint16_t* k_in, uint8_t* k_out, uint16_t* k_scales,
     }
 }
 
+/* [Cache] Description / Signature of q_to_fp16_kv: the inverse over the
+ * same rows. */
 void orc_q_to_fp16_kv(const uint8_t* k_in, uint16_t* k_out, const uint16_t* k_scales,
                       const uint8_t* v_in, uint16_t* v_out, const uint16_t* v_scales,
                       int dim0, int dim1, int heads, int head_dim,
@@ -343,7 +366,8 @@ void orc_q_to_fp16_kv(const uint8_t* k_in, uint16_t* k_out, const uint16_t* k_sc
     }
 }
 
-/* fp16 <-> 8-bit over the contiguous window rows (b, offset .. offset+width). */
+/* fp16 <-> 8-bit over the contiguous window rows (b, offset .. offset+width):
+ * [Cache] Description / Signature of fp16_to_fp8 and fp8_to_fp16. */
 void orc_fp16_to_fp8_cache(const uint16_t* in, uint8_t* out, int dim0, int dim1,
                            int heads, int head_dim, int batch_size, int offset, int width)
 {
@@ -372,6 +396,7 @@ void orc_fp8_to_fp16_cache(const uint8_t* in, uint16_t* out, int dim0, int dim1,
 
 /* ------------------------------------------------------------------------ */
 /* Matching prefix length, one element at a time (elements of 4 or 8 bytes). */
+/* [Cache] Description of count_match, with the element reading above.      */
 /* ------------------------------------------------------------------------ */
 
 int64_t orc_count_match(const void* a, int64_t len_a, const void* b, int64_t len_b,
@@ -412,6 +437,9 @@ void orc_scale_array(const uint16_t* a_bits, int64_t n, int wbits, uint16_t* out
 /* ------------------------------------------------------------------------ */
 /* Per-tensor formats (K and V may differ) and the full-prefix dequantize.   */
 /* fmt 0 = 8-bit high byte (no scales); 4, 6, 8 = block codes + fp16 scales. */
+/* Extensions of [Cache]'s operations (its Usage section names 8-bit caching */
+/* and Q4, Q6 and Q8 cache classes): the per-row rules above, with a format  */
+/* chosen per tensor.                                                        */
 /* ------------------------------------------------------------------------ */
 
 static void orc_narrow_row(const uint16_t* x, int64_t R, int fmt, uint8_t* out, uint16_t* scales)
@@ -534,7 +562,9 @@ void orc_kv_to_fp16_prefix(const uint8_t* k_in, uint16_t* k_out, const uint16_t*
     }
 }
 
-/* Bytes one token occupies in one cache tensor of a format:
+/* Bytes one token occupies in one cache tensor of a format (the capacity
+ * arithmetic of the llama.cpp tensor-split planning page, applied to these
+ * formats):
  * 16 = fp16, 0 = 8-bit high byte, 4/6/8 = block codes + one fp16 per 32. */
 int64_t orc_bytes_per_token(int fmt, int heads, int head_dim)
 {
