@@ -66,6 +66,12 @@ def load_library():
             raise RuntimeError(
                 "libkvq.so is not built (%s); run kv_cache_quantization_kvq_amd._build.build()"
                 % _build.LIB)
+        # torch ships its own HIP runtime (libamdhip64, same soname as the
+        # system one libkvq.so is linked against).  Loading torch first makes
+        # the library bind to that runtime; loaded the other way round, the
+        # process would hold two HIP runtimes, and the tensors and streams the
+        # binding passes would belong to the one the kernels are not launched on.
+        _torch()
         L = ctypes.CDLL(_build.LIB)
         q_args = [_vp, _vp, _vp, _vp, _vp, _vp, Shape, _i, _i, _i, _i, _vp, _vp, _i, _i, _vp]
         sig = {
