@@ -346,6 +346,53 @@ def test_randomized_configs(kvq):
         byte_diff(host(vo), ovo.view(np.uint16), what + " V fp16")
 
 
+def test_randomized_single_width(kvq):
+    """1000 seeded small configurations through the one-width entry points
+    (kvq_fp16_to_q_kv / kvq_q_to_fp16_kv; the page's fp16_to_q_kv and
+    q_to_fp16_kv): contiguous windows and paged tables with invalid entries
+    and out-of-range positions, wbits 4, 6 or 8, K and V together or one of
+    them, against the oracle, every byte of every buffer."""
+    t = torch()
+    rng = np.random.default_rng(20261204)
+    case = 0
+    while case < 1000:
+        c = _random_case(rng)
+        if c["mode"] == "prefix":
+            continue
+        wb = int(rng.choice([4, 6, 8]))
+        shape = c["shape"]
+        has_k, has_v = "k" in c["present"], "v" in c["present"]
+        what = "single-width case %d %s %s Q%d %s" % (case, c["mode"], shape, wb, c["present"])
+        case += 1
+        kq, vq = sentinel(_cshape(shape, wb), t.uint8), sentinel(_cshape(shape, wb), t.uint8)
+        ks, vs = sentinel(_sshape(shape), t.float16), sentinel(_sshape(shape), t.float16)
+        ko, vo = sentinel(shape, t.float16), sentinel(shape, t.float16)
+        okq, ovq = sentinel_np(_cshape(shape, wb), np.uint8), sentinel_np(_cshape(shape, wb), np.uint8)
+        oks, ovs = sentinel_np(_sshape(shape), np.float16), sentinel_np(_sshape(shape), np.float16)
+        oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+        kd, vd = dev(c["k"]), dev(c["v"])
+        sld = dev(c["sl"]) if c["sl"] is not None else None
+        btd = dev(c["bt"]) if c["bt"] is not None else None
+        a = (c["batch"], c["offset"], c["width"], c["ps"], sld, btd)
+        kt = (kd, kq, ks) if has_k else (None, None, None)
+        vt = (vd, vq, vs) if has_v else (None, None, None)
+        kvq.kvq_fp16_to_q_kv(*kt, *vt, *a, wbits=wb)
+        kvq.kvq_q_to_fp16_kv(*((kq, ko, ks) if has_k else (None,) * 3), *((vq, vo, vs) if has_v else (None,) * 3),
+                             *a, wbits=wb)
+        oa = (c["batch"], c["offset"], c["width"], c["ps"], c["sl"], c["bt"], wb)
+        okt = (c["k"], okq, oks) if has_k else (None, None, None)
+        ovt = (c["v"], ovq, ovs) if has_v else (None, None, None)
+        oracle.fp16_to_q_kv(*okt, *ovt, *oa)
+        oracle.q_to_fp16_kv(*((okq, oko, oks) if has_k else (None,) * 3),
+                            *((ovq, ovo, ovs) if has_v else (None,) * 3), *oa)
+        byte_diff(host(kq), okq, what + " K codes")
+        byte_diff(host(vq), ovq, what + " V codes")
+        byte_diff(host(ks), oks.view(np.uint16), what + " K scales")
+        byte_diff(host(vs), ovs.view(np.uint16), what + " V scales")
+        byte_diff(host(ko), oko.view(np.uint16), what + " K fp16")
+        byte_diff(host(vo), ovo.view(np.uint16), what + " V fp16")
+
+
 def test_every_entry_point_under_graph_capture(kvq):
     """One call of each device entry point captured in a single HIP graph:
     8-bit both ways, Q4 both ways, per-tensor (K Q6, V 8-bit) both ways and
