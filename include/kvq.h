@@ -21,6 +21,11 @@
  *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
  *     the default stream).  A kernel fault surfaces at the caller's next
  *     synchronisation with that stream.
+ *   - The library launches through the HIP runtime it is linked against
+ *     (libamdhip64.so.7).  Buffers and streams must come from the same runtime
+ *     instance: a program that also uses another copy of the runtime (torch
+ *     ships its own) must load that copy before this library, so that the
+ *     dynamic loader binds both to it.
  *   - A call enqueues exactly one kernel launch (none when it has nothing to
  *     do) and no memory set, copy, allocation or synchronisation, so it may
  *     be captured into a HIP graph; replays reread the tables' current
