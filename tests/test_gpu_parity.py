@@ -561,3 +561,55 @@ def test_paged_q4_concurrent_graph_chains(kvq):
     t.cuda.synchronize()
     for o, f, n in zip(outs, first, ("K codes", "K scales", "V codes", "V scales", "K out", "V out")):
         assert t.equal(o.view(t.uint8), f.view(t.uint8)), "second replay differs: %s" % n
+
+
+def test_concurrent_host_threads(kvq):
+    """Four host threads, each with its own stream and buffers, call the
+    library concurrently (20 paged Q4 round trips each, different tables per
+    thread); every thread's final bytes match the oracle."""
+    import threading
+    t = torch()
+    rng = np.random.default_rng(8080)
+    num_pages, ps, B, cols = 24, 8, 3, 4
+    shape = (num_pages, ps, 4, 128)
+    k = rng.standard_normal(shape).astype(np.float16)
+    v = (rng.standard_normal(shape) * 0.5).astype(np.float16)
+    kd, vd = dev(k), dev(v)
+    jobs = []
+    for i in range(4):
+        bt = rng.permutation(num_pages).astype(np.int32)[:B * cols].reshape(B, cols)
+        sl = rng.integers(0, cols * ps - 10, size=B).astype(np.int32)
+        outs = (sentinel(_cs(shape, 4), t.uint8), sentinel(_ss(shape), t.float16),
+                sentinel(_cs(shape, 4), t.uint8), sentinel(_ss(shape), t.float16),
+                sentinel(shape, t.float16), sentinel(shape, t.float16))
+        jobs.append((sl, bt, dev(sl), dev(bt), outs, t.cuda.Stream()))
+    t.cuda.synchronize()
+    errors = []
+
+    def work(job):
+        try:
+            sl, bt, sld, btd, (kq, ks, vq, vs, ko, vo), s = job
+            with t.cuda.stream(s):
+                for _ in range(20):
+                    kvq.kvq_fp16_to_q_kv(kd, kq, ks, vd, vq, vs, B, 0, 10, ps, sld, btd, 4)
+                    kvq.kvq_q_to_fp16_kv(kq, ko, ks, vq, vo, vs, B, 0, 10, ps, sld, btd, 4)
+            s.synchronize()
+        except Exception as e:        # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in jobs]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for i, (sl, bt, _, _, (kq, ks, vq, vs, ko, vo), _) in enumerate(jobs):
+        okq, ovq = sentinel_np(_cs(shape, 4), np.uint8), sentinel_np(_cs(shape, 4), np.uint8)
+        oks, ovs = sentinel_np(_ss(shape), np.float16), sentinel_np(_ss(shape), np.float16)
+        oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+        oracle.fp16_to_q_kv(k, okq, oks, v, ovq, ovs, B, 0, 10, ps, sl, bt, 4)
+        oracle.q_to_fp16_kv(okq, oko, oks, ovq, ovo, ovs, B, 0, 10, ps, sl, bt, 4)
+        for got, want, n in ((kq, okq, "K codes"), (ks, oks, "K scales"), (vq, ovq, "V codes"),
+                             (vs, ovs, "V scales"), (ko, oko, "K out"), (vo, ovo, "V out")):
+            byte_diff(host(got), want.view(np.uint8) if want.dtype != np.uint8 else want,
+                      "thread %d %s" % (i, n))
