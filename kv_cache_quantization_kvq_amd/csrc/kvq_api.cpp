@@ -23,6 +23,11 @@ using kvq::Fp8Launch;
 using kvq::QLaunch;
 
 constexpr int64_t kMaxRowElems = 1 << 20;
+// A launch's work-items per grid dimension (workgroups x threads) must fit
+// the 32-bit grid size of the dispatch packet; the bounds below keep every
+// launch under it with room for the last partial workgroup.
+constexpr int64_t kMaxWorkItems = (INT64_C(1) << 32) - 1024;
+constexpr int64_t kMaxUnits = kMaxWorkItems / 64;       // one 64-lane wavefront per unit
 constexpr int64_t kMaxCacheElems = INT64_C(1) << 60;    // dim0 * dim1 * heads * head_dim
 
 // a * b for a, b >= 0, saturated at INT64_MAX (extents of the overlap check)
@@ -85,7 +90,7 @@ int fp8_call(bool to_fp8, const void* in, void* out, kvq_shape s, int batch_size
     const int64_t elems = (int64_t)s.dim0 * s.dim1 * R;
     const Extent ext[2] = {{in, elems * (to_fp8 ? 2 : 1), false}, {out, elems * (to_fp8 ? 1 : 2), true}};
     if (any_output_overlap(ext, 2)) return KVQ_ERR_OVERLAP;
-    if ((int64_t)width * R / 8 / 1024 >= INT32_MAX) return KVQ_ERR_RANGE;   // grid.x bound
+    if ((int64_t)width * R / 8 > kMaxWorkItems) return KVQ_ERR_RANGE;   // one thread per 8 elements at most
     if (batch_size == 0 || width == 0) return KVQ_OK;
     Fp8Launch a;
     a.in = in;
@@ -148,10 +153,11 @@ int kv_call(CallKind kind, bool to_compact, const void* k_src, void* k_dst, cons
         if (!aligned(cache_seqlens, 4) || !aligned(block_table, 4)) return KVQ_ERR_ALIGN;
     }
     const int64_t R = (int64_t)s.heads * s.head_dim;
-    // work units (row segments of K and V) are numbered in 32 bits
+    // work units (row segments of K and V), one wavefront each
     const int64_t max_seg = (R / 8 + 63) / 64;
     const int64_t per_seq = kind == kPrefixWiden ? max_len : width;
-    if ((int64_t)batch_size * per_seq * 2 * max_seg > INT32_MAX / 2) return KVQ_ERR_RANGE;
+    if ((int64_t)batch_size * per_seq > kMaxUnits || (int64_t)batch_size * per_seq * 2 * max_seg > kMaxUnits)
+        return KVQ_ERR_RANGE;
     const void* ptrs[6] = {k_src, k_dst, k_scales, v_src, v_dst, v_scales};
     for (const void* p : ptrs)
         if (p && !aligned(p, 16)) return KVQ_ERR_ALIGN;
@@ -325,7 +331,7 @@ int kvq_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s16, int64
     if (nx < 0 || ns < 0 || nx % 8 != 0) return KVQ_ERR_RANGE;
     if (!aligned(x, 16) || !aligned(u_out, 16) || !aligned(s16, 2)) return KVQ_ERR_ALIGN;
     if (nx == 0 || ns == 0) return KVQ_OK;
-    if ((nx / 8) * ns > (int64_t)INT32_MAX * 64) return KVQ_ERR_RANGE;
+    if (nx / 8 > kMaxWorkItems / ns) return KVQ_ERR_RANGE;     // one thread per 8 x and scale
     return kvq::launch_selftest_codes(x, nx, s16, ns, wbits, force_clamp != 0, u_out, hip_stream)
                ? KVQ_ERR_HIP : KVQ_OK;
 }
@@ -333,7 +339,7 @@ int kvq_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s16, int64
 int kvq_selftest_scales(const uint16_t* absmax, int64_t n, int wbits, uint16_t* out, void* hip_stream) {
     if (wbits != 4 && wbits != 6 && wbits != 8) return KVQ_ERR_WBITS;
     if (!absmax || !out) return KVQ_ERR_NULL;
-    if (n < 0 || n > (int64_t)INT32_MAX * 64) return KVQ_ERR_RANGE;
+    if (n < 0 || n > kMaxWorkItems) return KVQ_ERR_RANGE;
     if (!aligned(absmax, 2) || !aligned(out, 2)) return KVQ_ERR_ALIGN;
     if (n == 0) return KVQ_OK;
     return kvq::launch_selftest_scales(absmax, n, wbits, out, hip_stream) ? KVQ_ERR_HIP : KVQ_OK;
@@ -341,7 +347,7 @@ int kvq_selftest_scales(const uint16_t* absmax, int64_t n, int wbits, uint16_t* 
 
 int kvq_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, uint32_t* q, void* hip_stream) {
     if (!n || !q) return KVQ_ERR_NULL;
-    if (d == 0 || d > (uint32_t)INT32_MAX || count < 0 || count > (int64_t)INT32_MAX * 64) return KVQ_ERR_RANGE;
+    if (d == 0 || d > (uint32_t)INT32_MAX || count < 0 || count > kMaxWorkItems) return KVQ_ERR_RANGE;
     if (!aligned(n, 4) || !aligned(q, 4)) return KVQ_ERR_ALIGN;
     if (count == 0) return KVQ_OK;
     return kvq::launch_selftest_fastdiv(n, count, d, q, hip_stream) ? KVQ_ERR_HIP : KVQ_OK;

@@ -165,6 +165,15 @@ def test_size_bounds(lib):
              quant=False) == RANGE
     f = lib.kvq_fp16_to_fp8
     assert f(A, A + GB, shp(d0=1, d1=2, h=8193, d=128), 0, 0, 2, None) == SHAPE
+    # a launch's work-items must fit 32 bits: batch * width * 2 tensors *
+    # ceil(R / 512) segments is at most 2^26 - 16 (R = 1024: 2 per row)
+    far3 = ((1 << 60), (2 << 60), (3 << 60))
+    far6 = ((4 << 60), (5 << 60), (6 << 60))
+    s_big = shp(d0=1 << 13, d1=1 << 12, h=8, d=128)
+    assert q(lib, s=s_big, k=far3, v=far6, batch=1 << 13, width=1 << 11) == RANGE     # 2^26
+    assert q(lib, s=s_big, k=far3, v=far6, batch=1 << 13, width=(1 << 11) - 1) != RANGE
+    assert f(1 << 60, 2 << 60, shp(d0=1, d1=1 << 25, h=8, d=128), 1, 0, 1 << 25, None) == RANGE
+    assert f(1 << 60, 2 << 60, shp(d0=1, d1=1 << 25, h=8, d=128), 1, 0, (1 << 25) - 8, None) != RANGE
     # a cache beyond 2^60 elements is RANGE, whatever the window
     big = shp(d0=(1 << 31) - 1, d1=(1 << 31) - 1, h=8, d=128)
     assert q(lib, s=big, batch=0) == RANGE
