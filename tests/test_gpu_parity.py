@@ -613,3 +613,23 @@ def test_concurrent_host_threads(kvq):
                              (vs, ovs, "V scales"), (ko, oko, "K out"), (vo, ovo, "V out")):
             byte_diff(host(got), want.view(np.uint8) if want.dtype != np.uint8 else want,
                       "thread %d %s" % (i, n))
+
+
+def test_fp8_batch_beyond_grid_y(kvq):
+    """The contiguous 8-bit calls cap the launch's second grid dimension at
+    65,535 sequences and loop over the rest: 70,000 sequences of one row
+    (window offset 1, width 1 of 2 rows, 8 elements per row) against the
+    oracle, untouched rows included."""
+    t = torch()
+    rng = np.random.default_rng(70000)
+    shape = (70000, 2, 1, 8)
+    x = rng.standard_normal(shape).astype(np.float16)
+    o8 = sentinel(shape, t.uint8)
+    ob = sentinel(shape, t.float16)
+    kvq.kvq_fp16_to_fp8(dev(x), o8, 70000, 1, 1)
+    kvq.kvq_fp8_to_fp16(o8, ob, 70000, 1, 1)
+    w8, wb = sentinel_np(shape, np.uint8), sentinel_np(shape, np.float16)
+    oracle.fp16_to_fp8(x, w8, 70000, 1, 1)
+    oracle.fp8_to_fp16(w8, wb, 70000, 1, 1)
+    byte_diff(host(o8), w8, "8-bit, 70,000 sequences")
+    byte_diff(host(ob), wb.view(np.uint16), "fp16 back, 70,000 sequences")
