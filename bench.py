@@ -553,6 +553,11 @@ def secondary_workloads(torch, kvq, synth, wl):
                           ("to_fp16", lambda _: kvq.kvq_fp8_to_fp16(o8, ob, 1, 0, 256), [0])], 64)
     nb = 256 * ROW * 3
     out["fp8_contig_hot"] = {k: {"us": round(v * 1e6, 2), "GB/s": round(nb / v / 1e9, 1)} for k, v in kt.items()}
+    # the launch floor these small launches sit on: a one-element fill,
+    # timed the same way (graph of back-to-back launches)
+    one = t.zeros(1, dtype=t.float32, device="cuda")
+    kt = time_kernels(t, [("fill", lambda _: one.fill_(1.0), [0])], 64)
+    out["launch_floor"] = {"us": round(kt["fill"] * 1e6, 2), "what": "one-element fill, graph of 64 launches"}
     for name, fn, wb in (("q4_contig_hot", synth.q4_contig, 4), ("q6_contig_hot", synth.q6_contig, 6)):
         cw = fn()
         k, v = t.from_numpy(cw.k).cuda(), t.from_numpy(cw.v).cuda()
