@@ -2,19 +2,47 @@
 // with the undefined-behaviour sanitizer: the argument validation and the
 // host count_match run as built, and any call that would reach a kernel
 // launch returns an error instead (the validation tests never get there).
+//
+// The stand-ins also check what the validation admitted: a launch the real
+// launcher would build with more work-items in a grid dimension than a
+// dispatch's 32-bit grid size holds aborts the process (K/V calls: one
+// 64-lane wavefront per row segment of at least 512 elements; 8-bit calls:
+// one thread per 8 elements at most).
+#include <stdlib.h>
+
 #include "../kv_cache_quantization_kvq_amd/csrc/kvq_internal.h"
 
 namespace kvq {
 
 static int no_device() { return 1; }
 
-int launch_fp16_to_fp8(const Fp8Launch&, void*) { return no_device(); }
-int launch_fp8_to_fp16(const Fp8Launch&, void*) { return no_device(); }
-int launch_quant_kv(const QLaunch&, void*) { return no_device(); }
-int launch_dequant_kv(const QLaunch&, void*) { return no_device(); }
-int launch_fp16_to_kv(const QLaunch&, void*) { return no_device(); }
-int launch_kv_to_fp16(const QLaunch&, void*) { return no_device(); }
-int launch_kv_to_fp16_prefix(const QLaunch&, void*) { return no_device(); }
+static int64_t mul_or_abort(int64_t a, int64_t b) {
+    int64_t r;
+    if (__builtin_mul_overflow(a, b, &r)) abort();
+    return r;
+}
+
+static int kv_launch(const QLaunch& a, bool prefix) {
+    const int64_t per_seq = prefix ? a.max_len : a.width;
+    const int64_t tensors = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
+    const int64_t segments = (a.R + 511) / 512;
+    const int64_t units = mul_or_abort(mul_or_abort(mul_or_abort(a.batch, per_seq), tensors), segments);
+    if (mul_or_abort(units, 64) >= (INT64_C(1) << 32)) abort();
+    return no_device();
+}
+
+static int fp8_launch(const Fp8Launch& a) {
+    if (a.span_elems / 8 >= (INT64_C(1) << 32)) abort();
+    return no_device();
+}
+
+int launch_fp16_to_fp8(const Fp8Launch& a, void*) { return fp8_launch(a); }
+int launch_fp8_to_fp16(const Fp8Launch& a, void*) { return fp8_launch(a); }
+int launch_quant_kv(const QLaunch& a, void*) { return kv_launch(a, false); }
+int launch_dequant_kv(const QLaunch& a, void*) { return kv_launch(a, false); }
+int launch_fp16_to_kv(const QLaunch& a, void*) { return kv_launch(a, false); }
+int launch_kv_to_fp16(const QLaunch& a, void*) { return kv_launch(a, false); }
+int launch_kv_to_fp16_prefix(const QLaunch& a, void*) { return kv_launch(a, true); }
 int launch_selftest_codes(const uint16_t*, int64_t, const uint16_t*, int64_t, int, bool, uint8_t*, void*) {
     return no_device();
 }

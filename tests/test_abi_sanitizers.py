@@ -3,7 +3,13 @@ arithmetic at extreme sizes, count_match) built with g++ and the address and
 undefined-behaviour sanitizers, aborting on the first report, and driven by
 the host-side ABI tests in a Python process that preloads the address
 sanitizer's runtime.  The kernel launchers are replaced by stand-ins that
-return an error (tests/host_launch_stub.cpp); no test reaches them."""
+return an error (tests/host_launch_stub.cpp); no test reaches them.  Then
+20,000 random-argument calls of every entry point (tests/abi_fuzz.py) run
+against the same build, and 5,000 calls that pass every check but the size
+bound, with windows up to 2^28 rows: every call returns a documented code,
+the sanitizers see no undefined behaviour in the validation arithmetic, and
+no call the validation admits would launch more work-items than a dispatch's
+32-bit grid size holds (the stand-in launchers check)."""
 import os
 import shutil
 import subprocess
@@ -26,7 +32,12 @@ import kv_cache_quantization_kvq_amd as kvq
 kvq._build.LIB = {lib!r}
 kvq._LIB = None
 import pytest
-sys.exit(pytest.main(["-q", "-s", "-p", "no:cacheprovider", {test_file!r}, "-k", {tests_k!r}]))
+rc = pytest.main(["-q", "-s", "-p", "no:cacheprovider", {test_file!r}, "-k", {tests_k!r}])
+if rc == 0:
+    import abi_fuzz
+    print("fuzz: %d random calls" % abi_fuzz.fuzz(kvq.load_library()), flush=True)
+    print("fuzz: %d large valid calls reached a launcher" % abi_fuzz.fuzz_valid(kvq.load_library()), flush=True)
+sys.exit(rc)
 """
 
 
@@ -49,3 +60,5 @@ def test_host_abi_under_sanitizers(tmp_path):
                                   UBSAN_OPTIONS="print_stacktrace=1"))
     assert out.returncode == 0, "exit %d\n%s\n%s" % (out.returncode, out.stdout[-3000:], out.stderr[-3000:])
     assert " passed" in out.stdout
+    assert "fuzz: 20000 random calls" in out.stdout
+    assert "large valid calls reached a launcher" in out.stdout
