@@ -10,13 +10,17 @@ launch).  The ExLlamaV2 cache page describes these operations
 example).
 
 Cold data: 32 seeded (cache_seqlens, block_table) draws are rotated, so each
-step touches rows the previous 31 steps did not (about 1.4 GB between reuses,
-beyond the 256 MB last-level cache).  The timed region replays HIP graphs of
-the steps (launch overhead off the host) between device synchronisations.
+launch touches rows the previous 31 did not (about 1.4 GB between reuses,
+beyond the 256 MB last-level cache).  The timed job is K quantize launches
+over the rotated draws, then K dequantize launches (quantized data is not
+cache-resident when it is read back), each replayed as HIP graphs between
+device synchronisations and timed with HIP events.
 
-Output: one JSON line (metric, value = algorithmic GB/s of the whole job,
-ms_per_step, roofline of the dominant kernel measured with HIP events,
-cpu_baseline = the CPU oracle on a bounded sample, timed on the host cores).
+Output: one JSON line: value = algorithmic bytes of the K steps / (quantize
++ dequantize kernel time), the roofline of the slower kernel, cpu_baseline
+= the CPU oracle on a bounded sample timed on the host cores, and secondary
+figures (the whole job on concurrent step chains, a plain-copy floor at the
+same launch size, the other formats and layouts).
 
 (The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
 Exllamav2 Ext Cache".)
@@ -24,6 +28,7 @@ Exllamav2 Ext Cache".)
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -50,11 +55,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=6400)
     p.add_argument("--warmup", type=int, default=64)
-    p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
-    p.add_argument("--graph-steps", type=int, default=20 * DRAWS,
-                   help="steps per captured graph (each replay forks and joins the chains)")
+    p.add_argument("--graph-steps", type=int, default=4 * DRAWS,
+                   help="launches per captured graph of the timed regions")
+    p.add_argument("--chain-graph-steps", type=int, default=20 * DRAWS,
+                   help="steps per captured graph of the whole-job figure")
     p.add_argument("--streams", type=int, default=3,
-                   help="independent step chains replayed concurrently (1 = strictly serial steps)")
+                   help="concurrent step chains of the whole-job figure (secondary.whole_job)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads' kernel timings")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -245,6 +251,88 @@ def oracle_detail(wl, oracle, rows_fn, kvq):
                             "library_us": round(t_lib * 1e6, 2)}}
 
 
+def capture_graph(torch, fn, n):
+    """A HIP graph of fn(0) .. fn(n - 1) launched back to back on one stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    return g
+
+
+def time_region(torch, fn, steps, per):
+    """`steps` launches fn(i % DRAWS), i < steps, replayed as graphs of `per`
+    back-to-back launches on the current stream, each replay between two
+    events; the region is bracketed by device synchronisation.  Returns
+    (median per-launch seconds over the replays, total seconds of the
+    region).  Inside a replay consecutive dispatches follow each other with
+    no measurable gap, so the per-launch time of a replay is the kernel's
+    own duration; the median discards the occasional replay that waits on
+    host-side submission."""
+    full, rem = steps // per, steps % per
+    distinct = DRAWS // math.gcd(per, DRAWS)              # replays r and r + distinct launch the same draws
+    graphs = [(capture_graph(torch, lambda i, r=r: fn((r * per + i) % DRAWS), per), per)
+              for r in range(min(full, distinct))]
+    g_rem = capture_graph(torch, lambda i: fn((full * per + i) % DRAWS), rem) if rem else None
+    for g, _ in graphs:
+        g.replay()                                        # untimed: graph upload
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    order = [graphs[r % len(graphs)] for r in range(full)] + ([(g_rem, rem)] if g_rem is not None else [])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i, (g, _) in enumerate(order):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e-3 / n for i, (_, n) in enumerate(order))
+    total = ev[0].elapsed_time(ev[-1]) * 1e-3
+    return per_launch[len(per_launch) // 2], total, wall
+
+
+def whole_job(torch, wl, steps, per, streams):
+    """Independent steps (quantize then dequantize of one draw) spread
+    round-robin over `streams` concurrent chains, graphs of `per` steps.
+    Steps of different draws touch different rows; two steps of one draw
+    write identical bytes to the same rows, so no result depends on how the
+    chains interleave.  Returns seconds for `steps` steps."""
+    chains = [torch.cuda.Stream() for _ in range(streams)]
+    for c in chains:
+        c.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+
+    def capture(n, first):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            for c in chains:
+                c.wait_stream(cap)                        # fork
+            for d in range(n):
+                with torch.cuda.stream(chains[d % streams]):
+                    wl.step((first + d) % DRAWS)
+            for c in chains:
+                cap.wait_stream(c)                        # join
+        return g
+
+    per = max(1, min(per, steps))
+    full, rem = steps // per, steps % per
+    graphs = [capture(per, 0)] if full else []
+    g_rem = capture(rem, full * per) if rem else None
+    for g in graphs + ([g_rem] if g_rem else []):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(full):
+        graphs[0].replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -252,8 +340,8 @@ def main():
               "converts independently; sharding by heads or sequences needs no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.steps < 1 or args.warmup < 0 or args.streams < 1 or args.graph_steps < 1:
-        print("bench.py: --steps, --streams and --graph-steps must be at least 1, --warmup at least 0",
+    if args.steps < 1 or args.warmup < 0 or args.streams < 1 or args.graph_steps < 1 or args.chain_graph_steps < 1:
+        print("bench.py: --steps, --streams and the graph sizes must be at least 1, --warmup at least 0",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -268,85 +356,40 @@ def main():
     dev_name = torch.cuda.get_device_name(0)
     wl = PagedKV(torch, kvq, synth, wbits=4)
 
-    # warmup (eager), also the parity reference for graph replays
-    for i in range(args.warmup):
+    # warmup: eager steps over the draws (every draw's codes exist before the
+    # dequantize region)
+    for i in range(max(args.warmup, DRAWS)):
         wl.step(i % DRAWS)
     torch.cuda.synchronize()
 
-    # graphs of `--graph-steps` steps spread round-robin over `--streams`
-    # independent chains.  Within a step, dequantize follows its quantize on
-    # the same chain.  Steps of different paging draws touch different rows;
-    # steps of one draw recur every DRAWS steps, and if two of them overlap on
-    # different chains they write identical bytes to the same rows, so no
-    # result depends on how the chains interleave.
-    graphs = None
-    if not args.no_graph:
-        chains = [torch.cuda.Stream() for _ in range(args.streams)]
-        for c in chains:
-            c.wait_stream(torch.cuda.current_stream())
-        for d in range(DRAWS):
-            with torch.cuda.stream(chains[d % args.streams]):
-                wl.step(d)
-        for c in chains:
-            torch.cuda.current_stream().wait_stream(c)
-        torch.cuda.synchronize()
+    # the timed job: K quantize launches over the rotated draws, then K
+    # dequantize launches (the cold-data protocol: quantized data is not
+    # cache-resident when it is read back)
+    per = max(1, min(args.graph_steps, args.steps))
+    log("timing %d quantize then %d dequantize launches (graphs of %d) on %s"
+        % (args.steps, args.steps, per, dev_name))
+    tq, tq_total, wq = time_region(torch, wl.quant, args.steps, per)
+    td, td_total, wd = time_region(torch, wl.dequant, args.steps, per)
+    # value: the algorithmic bytes of a step over the sum of the two kernels'
+    # per-launch times (the kernel-time definition of the metric)
+    value = wl.bytes_per_step / (tq + td) / 1e9
+    ms_per_step = (tq + td) * 1e3
 
-        def capture(n):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                cap = torch.cuda.current_stream()
-                for c in chains:
-                    c.wait_stream(cap)                       # fork
-                for d in range(n):
-                    with torch.cuda.stream(chains[d % args.streams]):
-                        wl.step(d % DRAWS)
-                for c in chains:
-                    cap.wait_stream(c)                       # join
-            return g
-
-        per = max(1, min(args.graph_steps, args.steps))
-        rem = args.steps % per
-        graphs = (capture(per), capture(rem) if rem else None)
-        graphs[0].replay()
-        torch.cuda.synchronize()
-
-    log("timing %d steps (%s) on %s" % (args.steps, "graph replay, %d chain(s)" % args.streams
-                                        if graphs else "eager", dev_name))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if graphs:
-        for _ in range(args.steps // per):
-            graphs[0].replay()
-        if graphs[1] is not None:
-            graphs[1].replay()
-    else:
-        for i in range(args.steps):
-            wl.step(i % DRAWS)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed / args.steps * 1e3
-    value = wl.bytes_per_step * args.steps / elapsed / 1e9
-
-    # per-kernel device durations (graph replays of each kernel alone)
-    reps = 4 * DRAWS
-    kt = time_kernels(torch, [("quant", wl.quant, list(range(DRAWS))),
-                              ("dequant", wl.dequant, list(range(DRAWS)))], reps)
-    dom = max(kt, key=kt.get)
+    kt = {"quant": tq, "dequant": td}
+    dom = max(kt, key=kt.get)                             # the slower kernel
     achieved = wl.bytes_per_launch / kt[dom] / 1e9
+    traffic, traffic_src = traffic_for(dom, wl.bytes_per_launch)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom, wl.bytes_per_launch),
-                "kernel": ("quant_kv_kernel<4>" if dom == "quant" else "dequant_kv_kernel<4>"),
-                "bytes_per_launch": wl.bytes_per_launch,
-                "avg_us": {k: round(v * 1e6, 3) for k, v in kt.items()}}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_source": traffic_src,
+                "kernel": KERNEL_NAMES[dom], "bytes_per_launch": wl.bytes_per_launch,
+                "avg_us": {k: round(v * 1e6, 3) for k, v in kt.items()},
+                "timing": "median over %d graph replays of %d back-to-back launches (rotated draws) "
+                          "of event time / launches" % (-(-args.steps // per), per),
+                "region_us_per_launch": {"quant": round(tq_total / args.steps * 1e6, 3),
+                                         "dequant": round(td_total / args.steps * 1e6, 3)}}
     # counter cross-check: HBM bytes the counters saw per launch over the same duration
-    roofline["counter_GBps"] = (round(roofline["traffic"] / kt[dom] / 1e9, 1)
-                                if roofline["traffic"] is not None else None)
-    # the pair figure: algorithmic bytes of one quantize and one dequantize
-    # launch over the sum of their kernel times (cold rows, serial launches)
-    pair_s = kt["quant"] + kt["dequant"]
-    kernel_pair = {"us": round(pair_s * 1e6, 3), "GB/s": round(2 * wl.bytes_per_launch / pair_s / 1e9, 1),
-                   "frac": round(2 * wl.bytes_per_launch / pair_s / 1e9 / HBM_PEAK_GBS, 4),
-                   "elements_per_s": round(2 * wl.elems_per_launch / pair_s, 1)}
+    roofline["counter_GBps"] = round(traffic / kt[dom] / 1e9, 1) if traffic is not None else None
 
     def rows_fn(t, rows):
         idx = torch.from_numpy(np.asarray(rows, np.int64)).cuda()
@@ -361,7 +404,6 @@ def main():
         import oracle
         log("timing the CPU oracle on %d draws" % args.cpu_draws)
         cb = cpu_baseline(wl, oracle, rows_fn, args.cpu_draws)
-        # the oracle's outputs against the device outputs of the same rows
         for d, name, rows, c, sc, y in cb["groups"]:
             q, s_, o = (wl.kq, wl.ks, wl.ko) if name == "K" else (wl.vq, wl.vs, wl.vo)
             if not (np.array_equal(rows_fn(q, rows), c) and np.array_equal(rows_fn(s_, rows), sc)
@@ -376,43 +418,95 @@ def main():
                          "scalar C oracle, rows split over %d threads, %.2f s wall"
                          % (cb["rows"], args.cpu_draws, cb["threads"], cb["seconds"])}
 
-    secondary = None if args.no_secondary else secondary_workloads(torch, kvq, synth, wl)
-    if secondary is not None:
-        def add_frac(d):
-            if isinstance(d, dict):
-                if "GB/s" in d:
-                    d["frac"] = round(d["GB/s"] / HBM_PEAK_GBS, 4)
-                for v in d.values():
-                    add_frac(v)
-        add_frac(secondary)
+    secondary = {}
+    t_wj = whole_job(torch, wl, args.steps, args.chain_graph_steps, args.streams)
+    secondary["whole_job"] = {"GB/s": round(wl.bytes_per_step * args.steps / t_wj / 1e9, 1),
+                              "us_per_step": round(t_wj / args.steps * 1e6, 3),
+                              "what": "%d steps (quantize then dequantize of one draw) on %d concurrent "
+                                      "chains, graphs of %d steps, host wall clock"
+                                      % (args.steps, args.streams, min(args.chain_graph_steps, args.steps))}
+    secondary["copy_floor"] = copy_floor(torch, kvq, wl.bytes_per_launch)
+    if not args.no_secondary:
+        secondary.update(secondary_workloads(torch, kvq, synth, wl))
+
+    def add_frac(d):
+        if isinstance(d, dict):
+            if "GB/s" in d:
+                d["frac"] = round(d["GB/s"] / HBM_PEAK_GBS, 4)
+            for v in d.values():
+                add_frac(v)
+    add_frac(secondary)
     if args.calibrate_copy:
         calibrate_copy(torch)
 
+    kernel_pair = {"us": round((tq + td) * 1e6, 3), "GB/s": round(value, 1), "frac": round(value / HBM_PEAK_GBS, 4),
+                   "elements_per_s": round(wl.elems_per_step / (tq + td), 1)}
     rec = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "arith": "fp16 data; fp32 quotients and scales (quantize), fp16 products (dequantize); "
+                    "4-bit codes",
            "data": "synthetic", "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-           "elements_per_s": round(wl.elems_per_step * args.steps / elapsed, 1),
+           "elements_per_s": round(wl.elems_per_step / (tq + td), 1),
            "config": {"workload": "paged_q4", "pages": wl.w.shape[0], "page_size": PAGE,
                       "heads": HEADS, "head_dim": HEAD_DIM, "batch": wl.w.batch_size,
                       "width": wl.w.width, "wbits": 4, "draws_rotated": DRAWS,
                       "bytes_per_step": wl.bytes_per_step,
-                      "timed": ("graphs of %d steps, %d chains" % (per, args.streams)) if graphs else "eager",
+                      "timed": "%d quantize launches then %d dequantize launches, graphs of %d launches, "
+                               "HIP events per replay; value = bytes per step / (quantize + dequantize "
+                               "per-launch kernel time)" % (args.steps, args.steps, per),
+                      "region_wall_s": round(wq + wd, 4),
                       "device": dev_name},
            "roofline": roofline, "kernel_pair": kernel_pair, "cpu_baseline": cpu}
     if cpu_detail is not None:
         rec["cpu_detail"] = cpu_detail
-    if secondary is not None:
-        rec["secondary"] = secondary
+    rec["secondary"] = secondary
     print(json.dumps(rec), flush=True)
 
 
+# kernel names of the paged-Q4 launches (rocprofv3 spelling)
+KERNEL_NAMES = {"quant": "kvq::narrow_pair_kernel<4, 1>",
+                "dequant": "kvq::widen_run_kernel<4, 1, 2, false, 4, 2>"}
+
+
+def copy_floor(torch, kvq, launch_bytes):
+    """A plain non-temporal copy moving the bytes of one paged-Q4 launch
+    (half read, half written), 32 rotated buffer pairs (cold), over bytes per
+    lane, waves per workgroup and one tile per wave against waves striding
+    inside one resident generation: the bandwidth one launch of this size
+    reaches without any conversion work."""
+    nbytes = launch_bytes // 2 // 16 * 16
+    src = torch.empty((DRAWS, nbytes), dtype=torch.uint8, device="cuda")
+    dst = torch.empty((DRAWS, nbytes), dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    out = {"bytes_moved": 2 * nbytes, "configs": []}
+    best = None
+    for lane_bytes in (16, 32, 64, 128):
+        for group_waves in (1, 2, 4):
+            for max_waves in (0, 4096):
+                fn = (lambda d, lb=lane_bytes, gw=group_waves, mw=max_waves:
+                      kvq.kvq_selftest_copy(src[d], dst[d], lb, gw, mw))
+                t = time_kernels(torch, [("copy", fn, list(range(DRAWS)))], 4 * DRAWS)["copy"]
+                tiles = -(-nbytes // (lane_bytes * 64))
+                row = {"lane_bytes": lane_bytes, "group_waves": group_waves,
+                       "waves": tiles if max_waves == 0 else min(tiles, max_waves),
+                       "us": round(t * 1e6, 3), "GB/s": round(2 * nbytes / t / 1e9, 1)}
+                out["configs"].append(row)
+                if best is None or t < best[0]:
+                    best = (t, row)
+    out["best"] = dict(best[1])
+    assert torch.equal(dst[DRAWS - 1], src[DRAWS - 1]), "copy floor: copy mismatch"
+    del src, dst
+    return out
+
+
 def traffic_for(kernel, algo_bytes):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources (else None)."""
+    """HBM bytes per launch from the committed counter summary and a label of
+    where they come from, or (None, reason) when the summary was taken on
+    other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic_paged_q4.txt")
     if not os.path.exists(path):
-        return None
+        return None, "no counter summary"
     kv = {}
     with open(path) as fh:
         for line in fh:
@@ -420,9 +514,12 @@ def traffic_for(kernel, algo_bytes):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
     if kv.get("sources_sha256") != sources_digest():
-        return None
+        return None, "profiles/traffic_paged_q4.txt was taken on other kernel sources"
     key = "%s_traffic_bytes_per_launch" % kernel
-    return float(kv[key]) if key in kv else None
+    if key not in kv:
+        return None, "no figure for this kernel"
+    return float(kv[key]), ("profiles/traffic_paged_q4.txt: rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch, "
+                            "each scaled by its reading for a 1 GiB copy (committed, same kernel sources)")
 
 
 def sources_digest():

@@ -42,11 +42,12 @@
  *   - Size limits: a row holds at most 2^20 elements (heads * head_dim), a
  *     cache at most 2^60 (dim0 * dim1 * heads * head_dim), a K/V call
  *     satisfies batch_size * width (max_len for the full prefix) * 2 *
- *     ceil(heads * head_dim / 512) <= 2^26 - 16, an 8-bit call converts at
+ *     ceil(heads * head_dim / 512) <= 2^26 - 64, an 8-bit call converts at
  *     most (2^32 - 1024) * 8 elements per sequence window, and a paged table
- *     spans block_table_cols * page_size < 2^31 positions.  (A K/V call runs
- *     one 64-lane wavefront per row segment of 512 or 1024 elements, and a
- *     launch's work-items must fit the 32-bit grid size of a dispatch.)
+ *     spans block_table_cols * page_size <= 2^30 positions.  (A K/V call runs
+ *     at most one 64-lane wavefront per row segment of 512 or 1024 elements,
+ *     a launch's work-items must fit the 32-bit grid size of a dispatch, and
+ *     the kernels test positions in 32-bit arithmetic.)
  *
  * Layouts (row = one token: heads * head_dim elements, R below)
  *   fp16 cache     [dim0, dim1, heads, head_dim]            uint16 (fp16 bits)

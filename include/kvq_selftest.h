@@ -56,6 +56,21 @@ KVQ_API int kvq_selftest_scales(const uint16_t* absmax, int64_t n, int wbits, ui
 KVQ_API int kvq_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, uint32_t* q,
                                  void* hip_stream);
 
+/*
+ * dst[0 .. bytes) = src[0 .. bytes) by a plain non-temporal copy kernel: the
+ * bandwidth reference the conversions are measured against (one launch of a
+ * given size, no conversion work).  A wave moves tiles of lane_bytes x 64
+ * bytes (lane_bytes / 16 loads of 16 bytes per lane, all issued before its
+ * stores); workgroups hold group_waves waves; with max_waves > 0 at most that
+ * many waves run and stride over the tiles, otherwise one wave per tile.
+ *   src, dst     device, 16-byte aligned, non-overlapping
+ *   bytes        >= 0, a multiple of 16
+ *   lane_bytes   16, 32, 64 or 128;  group_waves 1, 2, 4 or 8
+ * KVQ_ERR_RANGE / _ALIGN / _OVERLAP / _NULL before anything is enqueued.
+ */
+KVQ_API int kvq_selftest_copy(const void* src, void* dst, int64_t bytes, int lane_bytes, int group_waves,
+                              int64_t max_waves, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

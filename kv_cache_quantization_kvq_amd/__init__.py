@@ -24,7 +24,7 @@ from . import _build
 
 __all__ = ["KvqError", "kvq_fp16_to_fp8", "kvq_fp8_to_fp16", "kvq_fp16_to_q_kv",
            "kvq_q_to_fp16_kv", "kvq_count_match", "kvq_strerror", "kvq_version",
-           "kvq_selftest_codes", "kvq_selftest_scales", "kvq_selftest_fastdiv", "library_path", "load_library",
+           "kvq_selftest_codes", "kvq_selftest_scales", "kvq_selftest_fastdiv", "kvq_selftest_copy", "library_path", "load_library",
            "code_shape", "scale_shape", "kvq_fp16_to_kv", "kvq_kv_to_fp16", "kvq_kv_to_fp16_prefix",
            "kvq_bytes_per_token", "compact_shape", "KVQ_FMT_FP8", "KVQ_FMT_Q4", "KVQ_FMT_Q6",
            "KVQ_FMT_Q8", "KVQ_FMT_FP16"]
@@ -85,6 +85,7 @@ def load_library():
             "kvq_selftest_codes": (_i, [_vp, _i64, _vp, _i64, _i, _i, _vp, _vp]),
             "kvq_selftest_scales": (_i, [_vp, _i64, _i, _vp, _vp]),
             "kvq_selftest_fastdiv": (_i, [_vp, _i64, ctypes.c_uint32, _vp, _vp]),
+            "kvq_selftest_copy": (_i, [_vp, _vp, _i64, _i, _i, _i64, _vp]),
             "kvq_fp16_to_kv": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, Shape, _i, _i, _i, _i,
                                     _vp, _vp, _i, _vp]),
             "kvq_kv_to_fp16": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, Shape, _i, _i, _i, _i,
@@ -441,10 +442,13 @@ def kvq_selftest_codes(x_bits, s_bits, wbits, out, force_clamp=False, stream=Non
 
 
 def kvq_selftest_scales(a_bits, wbits, out, stream=None):
+    """out[i] = stored fp16 scale of a block with absmax a_bits[i] (device
+    16-bit tensors of the same shape)."""
     torch = _torch()
     dev = _device_of(a_bits)
     pa = _dev_ptr(a_bits.view(torch.int16), "absmax", torch.int16)
     po = _dev_ptr(out.view(torch.int16), "out", torch.int16, dev)
+    _expect_shape(out, tuple(a_bits.shape), "out")
     rc = load_library().kvq_selftest_scales(pa, a_bits.numel(), int(wbits), po,
                                             _stream_handle(stream, dev))
     _check(rc, "kvq_selftest_scales")
@@ -460,3 +464,17 @@ def kvq_selftest_fastdiv(n, d, out, stream=None):
     _expect_shape(out, tuple(n.shape), "out")
     rc = load_library().kvq_selftest_fastdiv(pn, n.numel(), int(d), po, _stream_handle(stream, dev))
     _check(rc, "kvq_selftest_fastdiv")
+
+
+def kvq_selftest_copy(src, dst, lane_bytes=16, group_waves=1, max_waves=0, stream=None):
+    """dst = src through the library's plain non-temporal copy kernel (device
+    uint8 tensors of equal size, a multiple of 16 bytes): the bandwidth
+    reference of one launch."""
+    torch = _torch()
+    dev = _device_of(src)
+    ps = _dev_ptr(src, "src", torch.uint8)
+    pd = _dev_ptr(dst, "dst", torch.uint8, dev)
+    _expect_shape(dst, tuple(src.shape), "dst")
+    rc = load_library().kvq_selftest_copy(ps, pd, src.numel(), int(lane_bytes), int(group_waves),
+                                          int(max_waves), _stream_handle(stream, dev))
+    _check(rc, "kvq_selftest_copy")

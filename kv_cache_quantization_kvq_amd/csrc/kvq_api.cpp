@@ -25,10 +25,14 @@ using kvq::QLaunch;
 constexpr int64_t kMaxRowElems = 1 << 20;
 // A launch's work-items per grid dimension (workgroups x threads) must fit
 // the 32-bit grid size of the dispatch packet; the bounds below keep every
-// launch under it with room for the last partial workgroup.
+// launch under it with room for the last partial workgroup and, for the K/V
+// calls, for padding the grid to a multiple of 8 workgroups.
 constexpr int64_t kMaxWorkItems = (INT64_C(1) << 32) - 1024;
-constexpr int64_t kMaxUnits = kMaxWorkItems / 64;       // one 64-lane wavefront per unit
+constexpr int64_t kMaxUnits = ((INT64_C(1) << 32) - 4096) / 64;   // at most one 64-lane wavefront per unit
 constexpr int64_t kMaxCacheElems = INT64_C(1) << 60;    // dim0 * dim1 * heads * head_dim
+// Positions a block-table row addresses (block_table_cols * page_size): the
+// kernels test positions in 32-bit arithmetic with this headroom.
+constexpr int64_t kMaxPositions = INT64_C(1) << 30;
 
 // a * b for a, b >= 0, saturated at INT64_MAX (extents of the overlap check)
 int64_t sat_mul(int64_t a, int64_t b) {
@@ -148,7 +152,7 @@ int kv_call(CallKind kind, bool to_compact, const void* k_src, void* k_dst, cons
     } else {
         if (page_size != s.dim1) return KVQ_ERR_SHAPE;
         if (batch_size < 0 || offset < 0 || width < 0 || block_table_cols <= 0) return KVQ_ERR_RANGE;
-        if ((int64_t)block_table_cols * page_size > INT32_MAX) return KVQ_ERR_RANGE;
+        if ((int64_t)block_table_cols * page_size > kMaxPositions) return KVQ_ERR_RANGE;
         if (!cache_seqlens || !block_table) return KVQ_ERR_NULL;
         if (!aligned(cache_seqlens, 4) || !aligned(block_table, 4)) return KVQ_ERR_ALIGN;
     }
@@ -351,6 +355,21 @@ int kvq_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, uint32_t*
     if (!aligned(n, 4) || !aligned(q, 4)) return KVQ_ERR_ALIGN;
     if (count == 0) return KVQ_OK;
     return kvq::launch_selftest_fastdiv(n, count, d, q, hip_stream) ? KVQ_ERR_HIP : KVQ_OK;
+}
+
+int kvq_selftest_copy(const void* src, void* dst, int64_t bytes, int lane_bytes, int group_waves,
+                      int64_t max_waves, void* hip_stream) {
+    if (!src || !dst) return KVQ_ERR_NULL;
+    if (bytes < 0 || bytes % 16 != 0 || max_waves < 0) return KVQ_ERR_RANGE;
+    if (lane_bytes != 16 && lane_bytes != 32 && lane_bytes != 64 && lane_bytes != 128) return KVQ_ERR_RANGE;
+    if (group_waves != 1 && group_waves != 2 && group_waves != 4 && group_waves != 8) return KVQ_ERR_RANGE;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return KVQ_ERR_ALIGN;
+    const Extent ext[2] = {{src, bytes, false}, {dst, bytes, true}};
+    if (any_output_overlap(ext, 2)) return KVQ_ERR_OVERLAP;
+    if (bytes / 16 > kMaxWorkItems) return KVQ_ERR_RANGE;      // at most one 16-byte element per work-item
+    if (bytes == 0) return KVQ_OK;
+    return kvq::launch_selftest_copy(src, dst, bytes / 16, lane_bytes, group_waves, max_waves, hip_stream)
+               ? KVQ_ERR_HIP : KVQ_OK;
 }
 
 }  // extern "C"

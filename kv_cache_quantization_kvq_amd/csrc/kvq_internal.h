@@ -73,5 +73,8 @@ int launch_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s, int6
                           int wbits, bool force_clamp, uint8_t* u, void* stream);
 int launch_selftest_scales(const uint16_t* a, int64_t n, int wbits, uint16_t* out, void* stream);
 int launch_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, uint32_t* q, void* stream);
+// Plain non-temporal copy of n16 16-byte elements (bandwidth reference).
+int launch_selftest_copy(const void* src, void* dst, int64_t n16, int lane_bytes, int group_waves, int64_t max_waves,
+                         void* stream);
 
 }  // namespace kvq

@@ -6,17 +6,27 @@
 // caches addressed through block_table / cache_seqlens).
 //
 // Work decomposition
-//   Contiguous 8-bit (the page's fp16_to_fp8 / fp8_to_fp16): each span (one
-//     sequence's window) is a contiguous run of width * R elements; threads
-//     stream 8-element chunks with 128-bit fp16 and 64-bit byte accesses.
-//   K/V conversions (Q4/Q6/Q8, and the per-tensor formats incl. paged
-//     8-bit): one wavefront per unit = (token row, tensor, row segment).
-//     fp16 -> compact: lane l owns 16 consecutive elements of the segment
-//     (1024 elements), so a 32-element block is a lane pair.  compact ->
-//     fp16: lane l holds 8-element chunks l and l + 64 of the segment, so
-//     each 128-bit store of the wave is contiguous.  The physical row is
-//     resolved once per wave from scalar loads of cache_seqlens /
-//     block_table.
+//   A "unit" is one 1024-element segment of one token row of one tensor
+//   (K or V); rows whose length R is not a multiple of 1024 end in a partial
+//   segment.  Token rows are (sequence b, position t < width) for the
+//   page's calls, or (b, position p < max_len) for the full-prefix widen.
+//
+//   fp16 -> compact (quantize, 8-bit narrow), R % 1024 == 0: one wavefront
+//     per pair of units of one tensor.  The wave reads its 4 KB of fp16 with
+//     contiguous 16-byte lanes, passes it through LDS, and lane L then owns
+//     32-element block L (unit L / 32): the absmax, scale and codes of a
+//     block are one lane's work, and each lane stores its block's codes with
+//     one 16/24/32-byte store.  8-bit narrowing needs no transpose.
+//   fp16 -> compact, other R: one wavefront per unit, lane l holding 16
+//     consecutive elements (a block is a lane pair).
+//   compact -> fp16 (dequantize, 8-bit widen, full-prefix widen): one
+//     wavefront per run of P consecutive positions of one sequence, both
+//     tensors (or one tensor when K and V formats differ).  Every load of
+//     the wave is issued before its first store; lane l converts chunks
+//     (8 elements) l and l + 64 of each unit, so every 128-bit store of the
+//     wave is contiguous.
+//   The paged row of a position is resolved from scalar loads of
+//   cache_seqlens[b] and block_table[b][p / page_size], once per run.
 //
 // (The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
 // Exllamav2 Ext Cache".)
@@ -25,10 +35,7 @@
 
 namespace kvq {
 
-#ifndef KVQ_WAVES_PER_BLOCK
-#define KVQ_WAVES_PER_BLOCK 4
-#endif
-constexpr int kWaves = KVQ_WAVES_PER_BLOCK;   // wavefronts per workgroup
+constexpr int kWaves = 4;                 // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 
 // ---------------------------------------------------------------- memory policy
@@ -37,11 +44,7 @@ constexpr int kThreads = 64 * kWaves;
 // codes, scales and bytes to widen back) are loaded, and all of its outputs
 // stored, with the non-temporal hint ("nt": streamed through the caches with
 // low retention).  A kernel's dirty L2 lines are written back when it ends,
-// so outputs that stream out during the kernel shorten its tail.  Measured
-// on MI355X at the paged Q4 workload (43 MB per launch, cold rows), against
-// ordinary stores: quantize 10.9 -> 10.2 us, dequantize 12.4 -> 11.0 us, and
-// a quantize + dequantize step 21.9 -> 21.2 us; the device-scope (sc0/sc1)
-// write-through policies were slower per kernel.
+// so outputs that stream out during the kernel shorten its tail.
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x3_t __attribute__((ext_vector_type(3), aligned(4)));
@@ -61,6 +64,7 @@ __device__ __forceinline__ void st_nt(uint2* p, uint2 v) {
     const u32x2_t w = {v.x, v.y};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
 }
+__device__ __forceinline__ void st_nt(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 // 12 bytes at a 4-byte aligned address
 __device__ __forceinline__ void st_nt3(void* p, uint32_t a, uint32_t b, uint32_t c) {
     const u32x3_t w = {a, b, c};
@@ -68,62 +72,87 @@ __device__ __forceinline__ void st_nt3(void* p, uint32_t a, uint32_t b, uint32_t
 }
 __device__ __forceinline__ void st_nt(uint16_t* p, uint32_t v) { __builtin_nontemporal_store((uint16_t)v, p); }
 
-// ---------------------------------------------------------------- row map
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+    return (__umulhi(n, f.mul) + n) >> f.shift;
+}
 
-// Launch geometry, computed by the host launcher for each call.
+// How positions map to cache rows.
+enum RowMode {
+    kContig = 0,   // position t of sequence b -> row (b, offset + t)
+    kPaged = 1,    // position t of sequence b -> cache position cache_seqlens[b] + offset + t
+    kPrefix = 2,   // position p of sequence b, live while p < cache_seqlens[b] + width
+};
+
+// Cache rows of NP positions t0 + d[k] of sequence b (d[k] in [0, NP); tin[k]
+// false: no position), or -1 when skipped.  Paged positions p live in page
+// block_table[b][p / page_size], slot p % page_size, and are skipped if
+// p < 0, past the table, or the page is outside [0, dim0).  All values are
+// wave-uniform (scalar loads and SALU).  The first position is clamped into
+// [-NP, lim] once (lim = bt_cols * page_size <= 2^30, a host bound), so
+// every per-position test is 32-bit and branch-free, and the block-table
+// loads of all NP positions issue together after the one load of
+// cache_seqlens[b].
+template <int MODE, int NP>
+__device__ __forceinline__ void resolve_positions(const QLaunch& a, FastDiv page_div, int32_t b, int32_t t0,
+                                                  const int32_t (&d)[NP], const bool (&tin)[NP],
+                                                  int64_t (&row)[NP]) {
+    if constexpr (MODE == kContig) {
+        const int64_t r0 = (int64_t)b * a.dim1 + a.offset + t0;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) row[k] = tin[k] ? r0 + d[k] : -1;
+    } else {
+        const int32_t sl = a.cache_seqlens[b];
+        const int32_t lim = a.bt_cols * a.page_size;
+        // prefix: positions from 0, live below cache_seqlens[b] + width
+        const int64_t p0l = (MODE == kPrefix ? 0 : (int64_t)sl + a.offset) + t0;
+        const int32_t p0 = (int32_t)(p0l < -NP ? -NP : (p0l > lim ? lim : p0l));
+        int32_t end = lim;
+        if (MODE == kPrefix) {
+            const int64_t e = (int64_t)sl + a.width;
+            end = (int32_t)(e < 0 ? 0 : (e > lim ? lim : e));
+        }
+        const int32_t* bt = a.block_table + (int64_t)b * a.bt_cols;
+        uint32_t pu[NP], pi[NP];
+        int32_t page[NP];
+        bool ok[NP];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int32_t p = p0 + d[k];
+            ok[k] = tin[k] & (p >= 0) & (p < end);
+            pu[k] = ok[k] ? (uint32_t)p : 0u;
+            pi[k] = fast_div(pu[k], page_div);
+            page[k] = bt[pi[k]];            // entry 0 for a skipped position (bt_cols >= 1)
+        }
+        // every entry is used whatever ok[k] says, so no load moves under a
+        // branch (each would then wait before the next issued)
+#pragma unroll
+        for (int k = 0; k < NP; ++k) page[k] = __builtin_amdgcn_readfirstlane(page[k]);
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const bool live = ok[k] & ((uint32_t)page[k] < (uint32_t)a.dim0);
+            row[k] = live ? (int64_t)page[k] * a.page_size + (int64_t)(pu[k] - pi[k] * (uint32_t)a.page_size) : -1;
+        }
+    }
+}
+
+// ================================================================ one unit per wave
+//
+// fp16 -> compact for rows whose length is not a multiple of 1024.  A unit
+// is (logical row n, tensor, segment g), numbered with the segment fastest,
+// then the tensor, then the row.  Lane l of segment g owns the 16
+// consecutive elements of piece pc = 64 g + l (two 128-bit loads); a
+// 32-element block is one lane pair, so the block absmax is one DPP
+// exchange.  GUARD masks the pieces past the row end of a partial last
+// segment (pieces per row are even, so a lane pair is in or out together).
+
 struct QGeom {
     int32_t n_units;   // rows * ntens * nseg
     int32_t nseg;      // row segments per row
     int32_t ntens;     // tensors present: 1 or 2
     int32_t tens0;     // the tensor when ntens == 1: 0 = K, 1 = V
-    FastDiv seq_div;   // logical rows per sequence: width (max_len for kPrefix)
+    FastDiv seq_div;   // logical rows per sequence: width
     FastDiv page_div;  // page_size (paged modes)
 };
-
-__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
-    return (__umulhi(n, f.mul) + n) >> f.shift;
-}
-
-// How logical rows map to cache rows.
-enum RowMode {
-    kContig = 0,   // n = b * width + t -> row (b, offset + t)
-    kPaged = 1,    // n = b * width + t -> position cache_seqlens[b] + offset + t
-    kPrefix = 2,   // n = b * max_len + p -> position p, live while p < cache_seqlens[b] + width
-};
-
-// Physical row of logical row n, or -1 when skipped.  Paged positions p live
-// in page block_table[b][p / page_size], slot p % page_size, and are skipped
-// if p < 0, past the table, or the page is outside [0, dim0).  All values
-// are wave-uniform (scalar loads and SALU).  The host bounds n and
-// bt_cols * page_size below 2^31, the domain of fast_div.
-template <int MODE>
-__device__ __forceinline__ int64_t resolve_row(const QLaunch& a, const QGeom& g, int32_t n) {
-    const int32_t per_seq = MODE == kPrefix ? a.max_len : a.width;
-    const int32_t b = (int32_t)fast_div((uint32_t)n, g.seq_div);
-    const int32_t t = n - b * per_seq;
-    if (MODE == kContig) return (int64_t)b * a.dim1 + a.offset + t;
-    int64_t p;
-    if (MODE == kPrefix) {
-        p = t;
-        if (p >= (int64_t)a.cache_seqlens[b] + a.width) return -1;
-    } else {
-        p = (int64_t)a.cache_seqlens[b] + a.offset + t;
-        if (p < 0) return -1;
-    }
-    if (p >= (int64_t)a.bt_cols * a.page_size) return -1;
-    const uint32_t pu = (uint32_t)p;
-    const uint32_t pi = fast_div(pu, g.page_div);
-    const int32_t page = a.block_table[(int64_t)b * a.bt_cols + pi];
-    if (page < 0 || page >= a.dim0) return -1;
-    return (int64_t)page * a.page_size + (int64_t)(pu - pi * (uint32_t)a.page_size);
-}
-
-// ---------------------------------------------------------------- work units
-//
-// A unit is one row segment of one tensor: (logical row n, tensor K or V,
-// segment g).  Units are numbered with the segment fastest, then the tensor,
-// then the row, so neighbouring waves share the row's paging lookup and
-// touch neighbouring memory.  One wavefront converts one unit.
 
 struct UnitRef {
     int64_t row;       // physical row (0 for a padding or skipped unit)
@@ -133,8 +162,7 @@ struct UnitRef {
 };
 
 // Dead units (grid padding past n_units, skipped rows) resolve to row 0 of
-// their tensor (always in bounds) with live == false; the kernels return
-// at once for them (a wave-uniform branch).
+// their tensor (always in bounds) with live == false.
 template <int MODE>
 __device__ __forceinline__ UnitRef unit_ref(const QLaunch& a, const QGeom& g, int32_t u) {
     UnitRef r;
@@ -154,23 +182,19 @@ __device__ __forceinline__ UnitRef unit_ref(const QLaunch& a, const QGeom& g, in
         n = rt;
         r.tensor = g.tens0;
     }
-    const int64_t row = resolve_row<MODE>(a, g, n);
-    r.live = r.live && row >= 0;
-    r.row = row >= 0 ? row : 0;
+    const int32_t b = (int32_t)fast_div((uint32_t)n, g.seq_div);
+    const int32_t d[1] = {0};
+    const bool tin[1] = {true};
+    int64_t row[1];
+    resolve_positions<MODE, 1>(a, g.page_div, b, n - b * a.width, d, tin, row);
+    r.live = r.live && row[0] >= 0;
+    r.row = row[0] >= 0 ? row[0] : 0;
     return r;
 }
 
 __device__ __forceinline__ int32_t wave_index() {
     return (int32_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
-
-// ---------------------------------------------------------------- fp16 -> compact
-//
-// Lane l of segment g owns the 16 consecutive elements of piece
-// pc = 64 g + l (two 128-bit loads); a 32-element block is one lane pair, so
-// the block absmax is one DPP exchange.  A segment is 1024 elements; GUARD
-// masks the pieces past the row end of a partial last segment (pieces per
-// row are even, so a lane pair is in or out together).
 
 // Pieces past the row end (in == false) read nothing and yield zeros.
 __device__ __forceinline__ void load_piece(const QLaunch& a, const UnitRef& ur, int32_t pc, bool in,
@@ -185,7 +209,6 @@ __device__ __forceinline__ void load_piece(const QLaunch& a, const UnitRef& ur, 
     }
 }
 
-// Block quantization of one unit.
 template <int WBITS, bool GUARD>
 __device__ __forceinline__ void quant_unit(const QLaunch& a, const UnitRef& ur, int lane) {
     const int32_t R = a.R;
@@ -225,7 +248,6 @@ __device__ __forceinline__ uint32_t high_bytes(uint32_t w0, uint32_t w1) {
     return __builtin_amdgcn_perm(w1, w0, 0x07050301u);
 }
 
-// 8-bit (high byte) narrowing of one unit: 16 bytes per lane.
 template <bool GUARD>
 __device__ __forceinline__ void narrow_unit(const QLaunch& a, const UnitRef& ur, int lane) {
     const int32_t pc = ur.seg * 64 + lane;
@@ -239,7 +261,7 @@ __device__ __forceinline__ void narrow_unit(const QLaunch& a, const UnitRef& ur,
 }
 
 template <int WBITS, int MODE, bool GUARD>
-__global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, QGeom g) {
+__global__ __launch_bounds__(kThreads) void quant_unit_kernel(QLaunch a, QGeom g) {
     const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
     if (!ur.live) return;   // wave-uniform: skipped rows and grid padding do nothing
     quant_unit<WBITS, GUARD>(a, ur, threadIdx.x & 63);
@@ -247,9 +269,9 @@ __global__ __launch_bounds__(kThreads) void quant_kv_kernel(QLaunch a, QGeom g) 
 
 // Per-tensor formats: the unit's tensor picks its format (wave-uniform).
 template <int MODE, bool GUARD>
-__global__ __launch_bounds__(kThreads) void narrow_kv_kernel(QLaunch a, QGeom g) {
+__global__ __launch_bounds__(kThreads) void narrow_unit_kernel(QLaunch a, QGeom g) {
     const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
-    if (!ur.live) return;   // wave-uniform: skipped rows and grid padding do nothing
+    if (!ur.live) return;
     const int lane = threadIdx.x & 63;
     switch (ur.tensor ? a.fmt_v : a.fmt_k) {
         case 4: quant_unit<4, GUARD>(a, ur, lane); break;
@@ -259,180 +281,356 @@ __global__ __launch_bounds__(kThreads) void narrow_kv_kernel(QLaunch a, QGeom g)
     }
 }
 
-// ---------------------------------------------------------------- compact -> fp16
+// ================================================================ wave-group geometry
 //
-// Lane l holds chunks (8 elements) c = NCH * 64 g + 64 k + l, k < NCH, so
-// every 128-bit store of the wave is contiguous.
+// Workgroups are dealt round-robin to the chip's 8 XCDs (each with its own
+// L2).  With XCD set, workgroup ids are renumbered so that each XCD takes one
+// contiguous range of groups: the waves sharing a sequence -- and its
+// cache_seqlens and block_table lines -- then share one L2.  The renumbering
+// is a bijection of [0, grid) for grids that are a multiple of 8 (the
+// launcher pads the grid).
+
+struct GroupGeom {
+    int32_t n_groups;
+    int32_t inner;       // groups per (sequence, tensor slot): position blocks x segments
+    FastDiv inner_div;
+    int32_t nseg;        // segments per row
+    FastDiv seg_div;
+    int32_t split;       // 1: one tensor per group, both present (tensor = (gid / inner) & 1)
+    int32_t tens0;       // the tensor when one tensor per group and only one present
+    int32_t xcd_per;     // workgroups per XCD (grid / 8) when renumbering by XCD, else 0
+    FastDiv page_div;
+};
+
+__device__ __forceinline__ int32_t group_index(const GroupGeom& g) {
+    const int32_t bid = (int32_t)blockIdx.x;
+    const int32_t xb = (bid & 7) * g.xcd_per + (bid >> 3);
+    return (g.xcd_per ? xb : bid) * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// group -> (sequence b, tensor of a one-tensor group, index within the
+// (sequence, tensor) slot); no branch, so every kernel-argument load of the
+// wave issues at once.  Padding groups (gid >= n_groups) take the last group
+// and are reported dead.
+__device__ __forceinline__ bool decode_group(const GroupGeom& g, int32_t& b, int32_t& tensor, int32_t& k) {
+    const int32_t raw = group_index(g);
+    const bool ok = raw < g.n_groups;
+    const int32_t gid = ok ? raw : g.n_groups - 1;
+    const int32_t rest = (int32_t)fast_div((uint32_t)gid, g.inner_div);
+    k = gid - rest * g.inner;
+    tensor = g.split ? (rest & 1) : g.tens0;
+    b = rest >> g.split;
+    return ok;
+}
+
+// ================================================================ fp16 -> compact, block per lane
+//
+// R % 1024 == 0.  A wave converts units u0 = 2k and u1 = 2k + 1 of one
+// (sequence, tensor): unit u is position u / nseg, segment u % nseg (u1 is
+// dead past the last unit).  Instruction i of the load loads chunk
+// c = 64 i + l (16 bytes) of the wave's 4 KB: unit i >> 1, chunk
+// (i & 1) * 64 + l of that unit.  Chunk c goes to LDS slot
+// (c & 3) * 66 + (c >> 2), so lane L later reads its block's chunks
+// 4L .. 4L + 3 from slots j * 66 + L (consecutive lanes, consecutive
+// slots); the stride of 66 keeps the 8 lanes of each write phase in
+// different banks.
+
+constexpr int kLdsSlots = 3 * 66 + 64;   // 16-byte slots per wave
+
+__device__ __forceinline__ uint32_t absmax_block(const uint4 (&v)[4]) {
+    u16x2_t m[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u16x2_t p = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v[i].x & 0x7FFF7FFFu),
+                                                    __builtin_bit_cast(u16x2_t, v[i].y & 0x7FFF7FFFu));
+        const u16x2_t q = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v[i].z & 0x7FFF7FFFu),
+                                                    __builtin_bit_cast(u16x2_t, v[i].w & 0x7FFF7FFFu));
+        m[i] = __builtin_elementwise_max(p, q);
+    }
+    const u16x2_t t = __builtin_elementwise_max(__builtin_elementwise_max(m[0], m[1]),
+                                                __builtin_elementwise_max(m[2], m[3]));
+    return (uint32_t)(t.x > t.y ? t.x : t.y);
+}
+
+// Codes of the block in v (32 elements, this lane), packed: Q4 in c[0..3],
+// Q6 in c[0..5] (two 12-byte groups of 16 codes), Q8 in c[0..7]; returns
+// the block's stored scale.
+template <int WBITS>
+__device__ __forceinline__ uint32_t quant_block(const uint4 (&v)[4], uint32_t (&c)[8]) {
+    const uint32_t s16 = scale_from_absmax<WBITS>(absmax_block(v));
+    const ScaleOps so = prep_scale(s16);
+    uint32_t u[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) quant_chunk<WBITS>(v[k], s16, so, u[k]);
+    if constexpr (WBITS == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = pack_q4(u[k]);
+        c[4] = c[5] = c[6] = c[7] = 0;
+    } else if constexpr (WBITS == 8) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            c[2 * k] = pack_q8x4(u[k][0], u[k][1], u[k][2], u[k][3]);
+            c[2 * k + 1] = pack_q8x4(u[k][4], u[k][5], u[k][6], u[k][7]);
+        }
+    } else {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pack_q6(u[k], lo[k], hi[k]);
+        c[0] = lo[0];
+        c[1] = __builtin_amdgcn_perm(lo[1], hi[0], 0x05040100u);   // hi0.lo16 | lo1.lo16 << 16
+        c[2] = __builtin_amdgcn_alignbit(hi[1], lo[1], 16);        // lo1 >> 16 | hi1 << 16
+        c[3] = lo[2];
+        c[4] = __builtin_amdgcn_perm(lo[3], hi[2], 0x05040100u);
+        c[5] = __builtin_amdgcn_alignbit(hi[3], lo[3], 16);
+        c[6] = c[7] = 0;
+    }
+    return s16;
+}
+
+// FMT: 0 (8-bit high byte), 4, 6 or 8 -- the format of the group's tensor.
+template <int FMT, int MODE>
+__device__ __forceinline__ void narrow_pair(const QLaunch& a, const GroupGeom& g, uint4 (*lds)[kLdsSlots],
+                                            bool gok, int32_t b, int32_t tensor, int32_t k) {
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int32_t R = a.R;
+    const int32_t units = a.width * g.nseg;
+    int32_t t[2], seg[2];
+    bool in[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int32_t u = 2 * k + h;
+        in[h] = u < units;
+        const int32_t uu = in[h] ? u : units - 1;
+        t[h] = (int32_t)fast_div((uint32_t)uu, g.seg_div);
+        seg[h] = uu - t[h] * g.nseg;
+    }
+    int64_t rr[2], row[2];
+    bool live[2];
+    const int32_t dt[2] = {0, t[1] - t[0]};   // 0 or 1: consecutive units
+    resolve_positions<MODE, 2>(a, g.page_div, b, t[0], dt, in, rr);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        live[h] = gok && rr[h] >= 0;
+        row[h] = rr[h] >= 0 ? rr[h] : 0;   // skipped units read row 0 and store nothing
+    }
+    const uint16_t* src = static_cast<const uint16_t*>(tensor ? a.v_src : a.k_src);
+    uint4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        x[i] = ld_nt(reinterpret_cast<const uint4*>(src + row[i >> 1] * R + seg[i >> 1] * 1024) + (i & 1) * 64 + lane);
+    if constexpr (FMT == 0) {
+        uint8_t* dst = static_cast<uint8_t*>(tensor ? a.v_dst : a.k_dst);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = i >> 1;
+            const uint2 d = make_uint2(high_bytes(x[i].x, x[i].y), high_bytes(x[i].z, x[i].w));
+            if (live[h]) st_nt(reinterpret_cast<uint2*>(dst + row[h] * R + seg[h] * 1024) + (i & 1) * 64 + lane, d);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 64 * i + lane;
+            lds[wv][(c & 3) * 66 + (c >> 2)] = x[i];
+        }
+        // the wave's own LDS writes are complete before it reads them back
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        uint4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = lds[wv][j * 66 + lane];
+        const int h = lane >> 5;
+        const int32_t blk = seg[h] * 32 + (lane & 31);
+        uint32_t c[8];
+        const uint32_t s16 = quant_block<FMT>(v, c);
+        constexpr int32_t seg_code_bytes = 128 * FMT;     // a 1024-element segment's codes
+        uint8_t* codes = static_cast<uint8_t*>(tensor ? a.v_dst : a.k_dst);
+        uint16_t* scales = static_cast<uint16_t*>(tensor ? a.v_scales : a.k_scales) + row[h] * (int64_t)(R >> 5);
+        if (live[h]) st_nt(scales + blk, s16);
+        if constexpr (FMT == 4) {
+            // 16 bytes per block: consecutive lanes, consecutive blocks
+            if (live[h])
+                st_nt(reinterpret_cast<uint4*>(codes + row[h] * (int64_t)(R / 2)) + blk, make_uint4(c[0], c[1], c[2], c[3]));
+        } else {
+            // 24 or 32 bytes per block: stage the wave's codes (unit 0 then
+            // unit 1, each seg_code_bytes) in its LDS and store them as
+            // contiguous 16-byte lanes
+            uint32_t* cw = reinterpret_cast<uint32_t*>(lds[wv]);
+            constexpr int W = FMT == 8 ? 8 : 6;           // dwords per block
+#pragma unroll
+            for (int i = 0; i < W; ++i) cw[lane * W + i] = c[i];
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            constexpr int pieces = 2 * seg_code_bytes / 16;   // 16-byte pieces of the wave's codes
+#pragma unroll
+            for (int i = 0; i < (pieces + 63) / 64; ++i) {
+                const int pc = 64 * i + lane;
+                if (pc < pieces) {
+                    const uint4 d = lds[wv][pc];
+                    const int uh = pc * 16 >= seg_code_bytes ? 1 : 0;
+                    const int32_t off = pc * 16 - uh * seg_code_bytes;
+                    const bool lv = uh ? live[1] : live[0];
+                    if (lv)
+                        st_nt(reinterpret_cast<uint4*>(codes + (uh ? row[1] : row[0]) * (int64_t)(R / 8 * FMT) +
+                                                       (int64_t)(uh ? seg[1] : seg[0]) * seg_code_bytes + off),
+                              d);
+                }
+            }
+        }
+    }
+}
+
+// Every present tensor has format FMT.
+template <int FMT, int MODE>
+__global__ __launch_bounds__(kThreads) void narrow_pair_kernel(QLaunch a, GroupGeom g) {
+    __shared__ uint4 lds[kWaves][kLdsSlots];
+    int32_t b, tensor, k;
+    const bool gok = decode_group(g, b, tensor, k);
+    narrow_pair<FMT, MODE>(a, g, lds, gok, b, tensor, k);
+}
+
+// ================================================================ compact -> fp16, runs of positions
+//
+// A group is (sequence b, block of P positions, segment) and NT tensors:
+// both (NT = 2) or one (NT = 1).  Lane l holds chunks (8 elements)
+// c = NCH * 64 * seg + 64 k + l, k < NCH, of each unit; GUARD masks the
+// chunks past the row end of a partial last segment.
 
 struct CodeChunk {
-    uint32_t lo, hi;    // Q4: lo = 8 codes; Q6: the 8 bytes holding the 6 code bytes; Q8: 8 codes
+    uint32_t lo, hi;    // Q4: lo = 8 codes; Q6: the 8 bytes holding the 6 code bytes; Q8 / 8-bit: 8 codes
     uint32_t s;         // scale (fp16 bits)
 };
 
-template <int WBITS>
+template <int FMT>
 __device__ __forceinline__ CodeChunk load_code_chunk(const uint8_t* __restrict__ codes_row,
-                                                     const uint16_t* __restrict__ scales_row,
-                                                     int32_t c) {
+                                                     const uint16_t* __restrict__ scales_row, int32_t c) {
     CodeChunk q;
-    if constexpr (WBITS == 4) {
+    if constexpr (FMT == 4) {
         q.lo = ld_nt(reinterpret_cast<const uint32_t*>(codes_row) + c);
         q.hi = 0;
-    } else if constexpr (WBITS == 8) {
-        const uint32_t* g = reinterpret_cast<const uint32_t*>(codes_row) + 2 * c;
-        q.lo = ld_nt(g);
-        q.hi = ld_nt(g + 1);
+    } else if constexpr (FMT == 8 || FMT == 0) {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(codes_row) + 2 * c;
+        q.lo = ld_nt(w);
+        q.hi = ld_nt(w + 1);
     } else {
         // chunk c's 6 bytes start at 6c: load the 8 bytes of its 12-byte
         // group that contain them (4-byte aligned); odd chunks are shifted
         // into place after the load.
-        const uint32_t* g = reinterpret_cast<const uint32_t*>(codes_row + 12 * (c >> 1) + 4 * (c & 1));
-        q.lo = ld_nt(g);
-        q.hi = ld_nt(g + 1);
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(codes_row + 12 * (c >> 1) + 4 * (c & 1));
+        q.lo = ld_nt(w);
+        q.hi = ld_nt(w + 1);
     }
-    q.s = ld_nt(scales_row + (c >> 2));
+    q.s = FMT == 0 ? 0u : ld_nt(scales_row + (c >> 2));
     return q;
-}
-
-// The codes of chunk c only (the caller supplies q.s).
-template <int WBITS>
-__device__ __forceinline__ CodeChunk load_code_only(const uint8_t* __restrict__ codes_row, int32_t c) {
-    CodeChunk q;
-    if constexpr (WBITS == 4) {
-        q.lo = ld_nt(reinterpret_cast<const uint32_t*>(codes_row) + c);
-        q.hi = 0;
-    } else if constexpr (WBITS == 8) {
-        const uint32_t* g = reinterpret_cast<const uint32_t*>(codes_row) + 2 * c;
-        q.lo = ld_nt(g);
-        q.hi = ld_nt(g + 1);
-    } else {
-        const uint32_t* g = reinterpret_cast<const uint32_t*>(codes_row + 12 * (c >> 1) + 4 * (c & 1));
-        q.lo = ld_nt(g);
-        q.hi = ld_nt(g + 1);
-    }
-    q.s = 0;
-    return q;
-}
-
-template <int WBITS>
-__device__ __forceinline__ uint4 dequant_chunk(const CodeChunk& q, int32_t c) {
-    const uint32_t s2 = q.s | (q.s << 16);
-    if constexpr (WBITS == 4) {
-        return dequant_q4_chunk(q.lo, s2);
-    } else if constexpr (WBITS == 8) {
-        return dequant_q8_chunk(q.lo, q.hi, s2);
-    } else {
-        uint32_t lo, hi;
-        if (c & 1) {
-            lo = __builtin_amdgcn_alignbit(q.hi, q.lo, 16);
-            hi = q.hi >> 16;
-        } else {
-            lo = q.lo;
-            hi = q.hi & 0xFFFFu;
-        }
-        return dequant_q6_chunk(lo, hi, s2);
-    }
-}
-
-// Block dequantization of one unit.  SSCALE: fetch the segment's scales
-// with one scalar load instead of per-lane loads (whole segments only).
-// Measured within one build at the paged workload (43 MB per launch): the
-// single-width Q4 kernel -2% and Q8 -5%, Q6 unchanged, and the per-tensor
-// kernel (format switch) +6%; so only the single-width Q4 and Q8 kernels
-// enable it.
-template <int WBITS, int NCH, bool GUARD, bool SSCALE>
-__device__ __forceinline__ void dequant_unit(const QLaunch& a, const UnitRef& ur, int lane) {
-    const int32_t R = a.R;
-    const int32_t cpr = R >> 3;
-    const uint8_t* codes = static_cast<const uint8_t*>(ur.tensor ? a.v_src : a.k_src) +
-                           ur.row * (int64_t)(R / 8 * WBITS);
-    const uint16_t* scales = static_cast<const uint16_t*>(ur.tensor ? a.v_scales : a.k_scales) +
-                             ur.row * (int64_t)(R >> 5);
-    CodeChunk q[NCH];
-    if constexpr (GUARD || !SSCALE) {
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
-            if (GUARD) q[k] = c < cpr ? load_code_chunk<WBITS>(codes, scales, c) : CodeChunk{0, 0, 0};
-            else q[k] = load_code_chunk<WBITS>(codes, scales, c);
-        }
-    } else {
-        // Whole segment: its NCH * 16 scales are NCH * 8 dwords inside the
-        // row, 32-byte aligned (R is a multiple of 512 here), fetched with one
-        // scalar load; lane l picks the scale of its chunks k * 64 + l (block
-        // (k * 64 + l) / 4: dword k * 8 + l / 8, half (l / 4) & 1).
-        const uint32_t* sw = reinterpret_cast<const uint32_t*>(scales) + ur.seg * (NCH * 8);
-        uint32_t S[NCH * 8];
-#pragma unroll
-        for (int i = 0; i < NCH * 8; ++i) S[i] = __builtin_amdgcn_readfirstlane(sw[i]);
-        const int32_t di = lane >> 3;
-        const bool hi = (lane >> 2) & 1;
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
-            q[k] = load_code_only<WBITS>(codes, c);
-            uint32_t w = S[k * 8];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) w = di == i ? S[k * 8 + i] : w;
-            q[k].s = hi ? (w >> 16) : (w & 0xFFFFu);
-        }
-    }
-    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * R);
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
-        const uint4 o = dequant_chunk<WBITS>(q[k], c);
-        if (ur.live && (!GUARD || c < cpr)) st_nt(dst + c, o);
-    }
 }
 
 // bytes 0,1 of w -> fp16 patterns byte << 8 in the low and high halves
 __device__ __forceinline__ uint32_t widen_lo(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x01040004u); }
 __device__ __forceinline__ uint32_t widen_hi(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x03040204u); }
 
-// 8-bit (high byte) widening of one unit.
-template <int NCH, bool GUARD>
-__device__ __forceinline__ void widen_unit(const QLaunch& a, const UnitRef& ur, int lane) {
+template <int FMT>
+__device__ __forceinline__ uint4 convert_chunk(const CodeChunk& q, int32_t c) {
+    if constexpr (FMT == 0) {
+        return make_uint4(widen_lo(q.lo), widen_hi(q.lo), widen_lo(q.hi), widen_hi(q.hi));
+    } else {
+        const uint32_t s2 = q.s | (q.s << 16);
+        if constexpr (FMT == 4) {
+            return dequant_q4_chunk(q.lo, s2);
+        } else if constexpr (FMT == 8) {
+            return dequant_q8_chunk(q.lo, q.hi, s2);
+        } else {
+            uint32_t lo, hi;
+            if (c & 1) {
+                lo = __builtin_amdgcn_alignbit(q.hi, q.lo, 16);
+                hi = q.hi >> 16;
+            } else {
+                lo = q.lo;
+                hi = q.hi & 0xFFFFu;
+            }
+            return dequant_q6_chunk(lo, hi, s2);
+        }
+    }
+}
+
+__device__ __forceinline__ int64_t code_row_bytes(int fmt, int32_t R) { return fmt == 0 ? R : (int64_t)(R / 8) * fmt; }
+
+template <int FMT, int MODE, int NCH, bool GUARD, int P, int NT>
+__device__ __forceinline__ void widen_run(const QLaunch& a, const GroupGeom& g, bool gok, int32_t b,
+                                          int32_t tsel, int32_t k) {
+    const int32_t per_seq = MODE == kPrefix ? a.max_len : a.width;
+    const int32_t tb = (int32_t)fast_div((uint32_t)k, g.seg_div);
+    const int32_t seg = k - tb * g.nseg;
+    int32_t d[P];
+    bool tin[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        d[p] = p;
+        tin[p] = tb * P + p < per_seq;
+    }
+    int64_t rr[P];
+    resolve_positions<MODE, P>(a, g.page_div, b, tb * P, d, tin, rr);
+    bool any = false;
+#pragma unroll
+    for (int p = 0; p < P; ++p) any = any || rr[p] >= 0;
+    if (!(gok && any)) return;   // wave-uniform: grid padding, or every position skipped
+    const int lane = threadIdx.x & 63;
     const int32_t R = a.R;
     const int32_t cpr = R >> 3;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(
-        static_cast<const uint8_t*>(ur.tensor ? a.v_src : a.k_src) + ur.row * (int64_t)R);
-    uint2 v[NCH];
+    CodeChunk q[P][NT][NCH];
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
-        v[k] = make_uint2(0, 0);
-        if (!GUARD || c < cpr) v[k] = make_uint2(ld_nt(src + 2 * c), ld_nt(src + 2 * c + 1));
-    }
-    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * R);
+    for (int p = 0; p < P; ++p) {
+        const int64_t row = rr[p] >= 0 ? rr[p] : 0;   // skipped positions read row 0 and store nothing
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        const int32_t c = ur.seg * (NCH * 64) + k * 64 + lane;
-        const uint4 o = make_uint4(widen_lo(v[k].x), widen_hi(v[k].x), widen_lo(v[k].y), widen_hi(v[k].y));
-        if (ur.live && (!GUARD || c < cpr)) st_nt(dst + c, o);
+        for (int j = 0; j < NT; ++j) {
+            const int tensor = NT == 2 ? j : tsel;
+            const uint8_t* codes = static_cast<const uint8_t*>(tensor ? a.v_src : a.k_src) + row * code_row_bytes(FMT, R);
+            const uint16_t* scales =
+                FMT == 0 ? nullptr : static_cast<const uint16_t*>(tensor ? a.v_scales : a.k_scales) + row * (int64_t)(R >> 5);
+#pragma unroll
+            for (int h = 0; h < NCH; ++h) {
+                const int32_t c = seg * (NCH * 64) + h * 64 + lane;
+                if (GUARD) q[p][j][h] = c < cpr ? load_code_chunk<FMT>(codes, scales, c) : CodeChunk{0, 0, 0};
+                else q[p][j][h] = load_code_chunk<FMT>(codes, scales, c);
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int tensor = NT == 2 ? j : tsel;
+            uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(tensor ? a.v_dst : a.k_dst) +
+                                                  (rr[p] >= 0 ? rr[p] : 0) * R);
+#pragma unroll
+            for (int h = 0; h < NCH; ++h) {
+                const int32_t c = seg * (NCH * 64) + h * 64 + lane;
+                const uint4 o = convert_chunk<FMT>(q[p][j][h], c);
+                if (rr[p] >= 0 && (!GUARD || c < cpr)) st_nt(dst + c, o);
+            }
+        }
     }
 }
 
-template <int WBITS, int MODE, int NCH, bool GUARD>
-__global__ __launch_bounds__(kThreads) void dequant_kv_kernel(QLaunch a, QGeom g) {
-    const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
-    if (!ur.live) return;   // wave-uniform: skipped rows and grid padding do nothing
-    dequant_unit<WBITS, NCH, GUARD, WBITS != 6>(a, ur, threadIdx.x & 63);
-}
-
-template <int MODE, int NCH, bool GUARD>
-__global__ __launch_bounds__(kThreads) void widen_kv_kernel(QLaunch a, QGeom g) {
-    const UnitRef ur = unit_ref<MODE>(a, g, wave_index());
-    if (!ur.live) return;   // wave-uniform: skipped rows and grid padding do nothing
-    const int lane = threadIdx.x & 63;
-    switch (ur.tensor ? a.fmt_v : a.fmt_k) {
-        case 4: dequant_unit<4, NCH, GUARD, false>(a, ur, lane); break;
-        case 6: dequant_unit<6, NCH, GUARD, false>(a, ur, lane); break;
-        case 8: dequant_unit<8, NCH, GUARD, false>(a, ur, lane); break;
-        default: widen_unit<NCH, GUARD>(a, ur, lane); break;
+// FMT >= 0: every present tensor has that format (0 = 8-bit); -1: per-tensor
+// formats, one tensor per group (NT == 1).
+template <int FMT, int MODE, int NCH, bool GUARD, int P, int NT>
+__global__ __launch_bounds__(kThreads) void widen_run_kernel(QLaunch a, GroupGeom g) {
+    int32_t b, tsel, k;
+    const bool gok = decode_group(g, b, tsel, k);
+    if constexpr (FMT >= 0) {
+        widen_run<FMT, MODE, NCH, GUARD, P, NT>(a, g, gok, b, tsel, k);
+    } else {
+        static_assert(NT == 1, "per-tensor formats take one tensor per group");
+        switch (tsel ? a.fmt_v : a.fmt_k) {   // wave-uniform
+            case 4: widen_run<4, MODE, NCH, GUARD, P, 1>(a, g, gok, b, tsel, k); break;
+            case 6: widen_run<6, MODE, NCH, GUARD, P, 1>(a, g, gok, b, tsel, k); break;
+            case 8: widen_run<8, MODE, NCH, GUARD, P, 1>(a, g, gok, b, tsel, k); break;
+            default: widen_run<0, MODE, NCH, GUARD, P, 1>(a, g, gok, b, tsel, k); break;
+        }
     }
 }
 
-// ---------------------------------------------------------------- 8-bit
+// ================================================================ contiguous 8-bit
 
 // Contiguous windows: each sequence's window is one run of width * R
 // elements, streamed 8 elements per chunk, CPT chunks per thread (4 for
@@ -484,11 +682,12 @@ __global__ __launch_bounds__(kThreads) void fp8_to_fp16_kernel(Fp8Launch a) {
     }
 }
 
-// ---------------------------------------------------------------- self-test kernels
+// ================================================================ self-test kernels
 
 // u[i * nx + j] = code of x[j] under scale s[i], through the same routines
-// as quant_kv_kernel (one thread per chunk of 8 x values).  CLAMP_ALL forces
-// the clamping path; otherwise the kernels' dispatch on the scale is used.
+// as the conversion kernels (one thread per chunk of 8 x values).
+// CLAMP_ALL forces the clamping path; otherwise the kernels' dispatch on the
+// scale is used.
 template <int WBITS, bool CLAMP_ALL>
 __global__ __launch_bounds__(kThreads) void selftest_codes_kernel(const uint16_t* __restrict__ x, int64_t nx,
                                                                   const uint16_t* __restrict__ s16,
@@ -523,7 +722,33 @@ __global__ __launch_bounds__(kThreads) void selftest_fastdiv_kernel(const uint32
     if (t < count) q[t] = fast_div(n[t], f);
 }
 
-// ---------------------------------------------------------------- launchers
+// Plain non-temporal copy of n16 16-byte elements: a wave moves tiles of
+// VPL x 64 consecutive elements (VPL loads per lane, all issued before its
+// stores); waves stride over the tiles when the grid is smaller than the
+// tile count.
+template <int VPL, int WPB>
+__global__ __launch_bounds__(64 * WPB) void selftest_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                                 int64_t n16) {
+    const int64_t nw = (int64_t)gridDim.x * WPB;
+    const int lane = threadIdx.x & 63;
+    const int64_t tiles = (n16 + VPL * 64 - 1) / (VPL * 64);
+    for (int64_t w = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6); w < tiles; w += nw) {
+        const int64_t base = w * (VPL * 64) + lane;
+        uint4 v[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int64_t i = base + k * 64;
+            v[k] = i < n16 ? ld_nt(src + i) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int64_t i = base + k * 64;
+            if (i < n16) st_nt(dst + i, v[k]);
+        }
+    }
+}
+
+// ================================================================ launchers
 
 static int launch(const void* fn, dim3 grid, dim3 block, void** args, void* stream) {
     return (int)hipLaunchKernel(fn, grid, block, args, 0, static_cast<hipStream_t>(stream));
@@ -562,116 +787,185 @@ int launch_fp8_to_fp16(const Fp8Launch& a, void* stream) {
     return launch(fn, fp8_grid(a, cpt), dim3(kThreads), args, stream);
 }
 
-// Kernel variants.  fp16 -> compact: 64 lanes x 16 elements per segment,
-// guarded when the row's 16-element pieces are not a multiple of 64.
-// compact -> fp16: NCH chunks of 8 per lane, NCH = 2 (or 1) when the row's
-// chunks are a multiple of 128 (or 64), else NCH = 2 guarded.  The
-// single-format kernels serve the page's one-wbits calls; the per-tensor
-// kernels pick each unit's format at run time.
-template <int W, int MODE>
-static const void* quant_fn(bool guard) {
-    return guard ? reinterpret_cast<const void*>(&quant_kv_kernel<W, MODE, true>)
-                 : reinterpret_cast<const void*>(&quant_kv_kernel<W, MODE, false>);
+// The common format of the present tensors, or -1 when K and V differ.
+static int common_format(const QLaunch& a) {
+    const int fk = a.k_src ? a.fmt_k : -1, fv = a.v_src ? a.fmt_v : -1;
+    if (fk < 0) return fv;
+    return (fv < 0 || fv == fk) ? fk : -1;
 }
 
-template <int MODE>
-static const void* narrow_fn(bool guard) {
-    return guard ? reinterpret_cast<const void*>(&narrow_kv_kernel<MODE, true>)
-                 : reinterpret_cast<const void*>(&narrow_kv_kernel<MODE, false>);
-}
-
-template <int W, int MODE>
-static const void* dequant_fn(int nch, bool guard) {
-    if (guard) return reinterpret_cast<const void*>(&dequant_kv_kernel<W, MODE, 2, true>);
-    if (nch == 2) return reinterpret_cast<const void*>(&dequant_kv_kernel<W, MODE, 2, false>);
-    return reinterpret_cast<const void*>(&dequant_kv_kernel<W, MODE, 1, false>);
-}
-
-template <int MODE>
-static const void* widen_fn(int nch, bool guard) {
-    if (guard) return reinterpret_cast<const void*>(&widen_kv_kernel<MODE, 2, true>);
-    if (nch == 2) return reinterpret_cast<const void*>(&widen_kv_kernel<MODE, 2, false>);
-    return reinterpret_cast<const void*>(&widen_kv_kernel<MODE, 1, false>);
-}
-
-template <int W>
-static const void* single_fn(bool to_compact, int mode, int nch, bool guard) {
-    if (to_compact) return mode == kPaged ? quant_fn<W, kPaged>(guard) : quant_fn<W, kContig>(guard);
-    if (mode == kPrefix) return dequant_fn<W, kPrefix>(nch, guard);
-    return mode == kPaged ? dequant_fn<W, kPaged>(nch, guard) : dequant_fn<W, kContig>(nch, guard);
-}
-
-static const void* mixed_fn(bool to_compact, int mode, int nch, bool guard) {
-    if (to_compact) return mode == kPaged ? narrow_fn<kPaged>(guard) : narrow_fn<kContig>(guard);
-    if (mode == kPrefix) return widen_fn<kPrefix>(nch, guard);
-    return mode == kPaged ? widen_fn<kPaged>(nch, guard) : widen_fn<kContig>(nch, guard);
-}
-
-// mixed: per-tensor formats (a.fmt_k / a.fmt_v); otherwise one width a.wbits
-static int launch_units(const QLaunch& a, bool to_compact, bool mixed, int mode, void* stream) {
-    int nch = 2;
-    bool guard = false;
-    int32_t seg_elems;
-    if (to_compact) {
-        guard = (a.R / 16) % 64 != 0;
-        seg_elems = 1024;
-    } else {
-        const int32_t cpr = a.R >> 3;
-        if (cpr % 128 == 0) nch = 2;
-        else if (cpr % 64 == 0) nch = 1;
-        else guard = true;
-        seg_elems = nch * 64 * 8;
+// xcd: renumber workgroups by XCD (the grid is padded to a multiple of 8)
+static int launch_groups(const void* fn, GroupGeom& g, bool xcd, QLaunch a, void* stream) {
+    if (!fn) return (int)hipErrorInvalidDeviceFunction;
+    int64_t grid = (g.n_groups + kWaves - 1) / kWaves;
+    g.xcd_per = 0;
+    if (xcd) {
+        grid = (grid + 7) / 8 * 8;
+        g.xcd_per = (int32_t)(grid / 8);
     }
-    const int64_t rows = (int64_t)a.batch * (mode == kPrefix ? a.max_len : a.width);
+    void* args[] = {&a, &g};
+    return launch(fn, dim3((unsigned)grid), dim3(kThreads), args, stream);
+}
+
+// ---------------------------------------------------------------- fp16 -> compact
+
+template <int MODE>
+static const void* narrow_pair_fn(int fmt) {
+    switch (fmt) {
+        case 0: return reinterpret_cast<const void*>(&narrow_pair_kernel<0, MODE>);
+        case 4: return reinterpret_cast<const void*>(&narrow_pair_kernel<4, MODE>);
+        case 6: return reinterpret_cast<const void*>(&narrow_pair_kernel<6, MODE>);
+        case 8: return reinterpret_cast<const void*>(&narrow_pair_kernel<8, MODE>);
+        default: return nullptr;   // no single format: the caller takes the one-unit kernel
+    }
+}
+
+template <int MODE>
+static const void* unit_fn(int fmt, bool guard) {
+    if (fmt == 4) return guard ? reinterpret_cast<const void*>(&quant_unit_kernel<4, MODE, true>)
+                               : reinterpret_cast<const void*>(&quant_unit_kernel<4, MODE, false>);
+    if (fmt == 6) return guard ? reinterpret_cast<const void*>(&quant_unit_kernel<6, MODE, true>)
+                               : reinterpret_cast<const void*>(&quant_unit_kernel<6, MODE, false>);
+    if (fmt == 8) return guard ? reinterpret_cast<const void*>(&quant_unit_kernel<8, MODE, true>)
+                               : reinterpret_cast<const void*>(&quant_unit_kernel<8, MODE, false>);
+    return guard ? reinterpret_cast<const void*>(&narrow_unit_kernel<MODE, true>)
+                 : reinterpret_cast<const void*>(&narrow_unit_kernel<MODE, false>);
+}
+
+static int launch_to_compact(const QLaunch& a, void* stream) {
+    const bool paged = a.page_size != 0;
+    const int fmt = common_format(a);
+    const int ntens = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
+    if (a.R % 1024 == 0 && fmt >= 0) {
+        // pairs of units of one tensor per wave (one format for the launch;
+        // K and V at different widths measured faster one unit per wave:
+        // 18.5 against 19.3 us for K-Q4 + V-Q6 at 64 x 256 positions)
+        GroupGeom g;
+        g.nseg = a.R / 1024;
+        g.seg_div = make_fastdiv((uint32_t)g.nseg);
+        const int64_t units = (int64_t)a.width * g.nseg;
+        g.inner = (int32_t)((units + 1) / 2);
+        g.inner_div = make_fastdiv((uint32_t)g.inner);
+        g.split = ntens == 2 ? 1 : 0;
+        g.tens0 = a.k_src ? 0 : 1;
+        g.n_groups = (int32_t)((int64_t)a.batch * ntens * g.inner);   // bounded by the host checks
+        g.page_div = make_fastdiv(paged ? (uint32_t)a.page_size : 1u);
+        const void* fn = paged ? narrow_pair_fn<kPaged>(fmt) : narrow_pair_fn<kContig>(fmt);
+        // XCD renumbering for launches of one resident generation (at the
+        // paged Q4 size: 9.66 against 9.72 us; at 65,536 contiguous Q6 units
+        // it costs 3%)
+        return launch_groups(fn, g, (int64_t)a.batch * ntens * units <= 16384, a, stream);
+    }
+    // one unit per wave: the row's 16-element pieces, guarded when they are
+    // not a multiple of 64
+    const bool guard = (a.R / 16) % 64 != 0;
     QGeom g;
-    g.nseg = (a.R + seg_elems - 1) / seg_elems;
-    g.ntens = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
+    g.nseg = (a.R + 1023) / 1024;
+    g.ntens = ntens;
     g.tens0 = a.k_src ? 0 : 1;
-    g.n_units = (int32_t)(rows * g.ntens * g.nseg);   // bounded by the host checks
-    g.seq_div = make_fastdiv((uint32_t)(mode == kPrefix ? a.max_len : a.width));
-    g.page_div = make_fastdiv(a.page_size > 0 ? (uint32_t)a.page_size : 1u);
+    g.n_units = (int32_t)((int64_t)a.batch * a.width * g.ntens * g.nseg);   // bounded by the host checks
+    g.seq_div = make_fastdiv((uint32_t)a.width);
+    g.page_div = make_fastdiv(paged ? (uint32_t)a.page_size : 1u);
     const dim3 grid((unsigned)((g.n_units + kWaves - 1) / kWaves));
     QLaunch arg = a;
     void* args[] = {&arg, &g};
-    // Per-tensor widening where every present tensor is Q4 (or every one
-    // Q8) runs the single-width kernel of that width: it has the scalar
-    // scale fetch, which the format-switch kernel does not take.
-    int wbits = a.wbits;
-    if (mixed && !to_compact) {
-        const int fk = a.k_src ? a.fmt_k : -1, fv = a.v_src ? a.fmt_v : -1;
-        const int f = fk < 0 ? fv : (fv < 0 || fv == fk ? fk : -1);
-        if (f == 4 || f == 8) {
-            mixed = false;
-            wbits = f;
-        }
-    }
     const void* fn;
-    if (mixed) fn = mixed_fn(to_compact, mode, nch, guard);
-    else if (wbits == 4) fn = single_fn<4>(to_compact, mode, nch, guard);
-    else if (wbits == 6) fn = single_fn<6>(to_compact, mode, nch, guard);
-    else fn = single_fn<8>(to_compact, mode, nch, guard);
+    if (fmt > 0) fn = paged ? unit_fn<kPaged>(fmt, guard) : unit_fn<kContig>(fmt, guard);
+    else fn = paged ? unit_fn<kPaged>(-1, guard) : unit_fn<kContig>(-1, guard);   // per-tensor switch (or 8-bit)
     return launch(fn, grid, dim3(kThreads), args, stream);
 }
 
-int launch_quant_kv(const QLaunch& a, void* stream) {
-    return launch_units(a, true, false, a.page_size ? kPaged : kContig, stream);
+// ---------------------------------------------------------------- compact -> fp16
+//
+// Runs of P = 4 positions with both tensors, or P = 8 positions of one
+// tensor, when that makes 1,024 to 2,048 waves (8,192 to 16,384 units): a
+// single resident generation whose waves each keep 8 units in flight, so
+// every lookup finishes before the chip's memory queues fill.  Other
+// launches take one position per wave: small ones to fill the chip, large
+// ones because many short waves stream better over several generations
+// (both tensors of a position in one wave when paged, sharing the lookup).
+// Measured at the paged Q4 size (16,384 units): 8.97 us for 4 positions x 2
+// tensors per wave with XCD renumbering, against 10.67 us for one position;
+// for the full-prefix widen of the same caches (~530,000 units): 135 us for
+// one position x 2 tensors, 148 us for 4 positions, 158 us with XCD
+// renumbering; contiguous Q6 at 65,536 units: 32.1 us for one unit per wave,
+// 33.3 us for two.
+
+template <int FMT, int MODE, int NCH, bool GUARD>
+static const void* widen_fn(int P, int NT) {
+    if (NT == 2) return P == 4 ? reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 4, 2>)
+                               : reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 1, 2>);
+    return P == 8 ? reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 8, 1>)
+                  : reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 1, 1>);
 }
+
+template <int MODE, int NCH, bool GUARD>
+static const void* widen_fn_fmt(int fmt, int P, int NT) {
+    switch (fmt) {
+        case 0: return widen_fn<0, MODE, NCH, GUARD>(P, NT);
+        case 4: return widen_fn<4, MODE, NCH, GUARD>(P, NT);
+        case 6: return widen_fn<6, MODE, NCH, GUARD>(P, NT);
+        case 8: return widen_fn<8, MODE, NCH, GUARD>(P, NT);
+        default:   // per-tensor formats: one tensor per group
+            return P == 8 ? reinterpret_cast<const void*>(&widen_run_kernel<-1, MODE, NCH, GUARD, 8, 1>)
+                          : reinterpret_cast<const void*>(&widen_run_kernel<-1, MODE, NCH, GUARD, 1, 1>);
+    }
+}
+
+template <int MODE>
+static const void* widen_fn_mode(int fmt, int nch, bool guard, int P, int NT) {
+    if (guard) return widen_fn_fmt<MODE, 2, true>(fmt, P, NT);
+    return nch == 2 ? widen_fn_fmt<MODE, 2, false>(fmt, P, NT) : widen_fn_fmt<MODE, 1, false>(fmt, P, NT);
+}
+
+static int launch_to_fp16(const QLaunch& a, int mode, void* stream) {
+    const int fmt = common_format(a);
+    const int ntens = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
+    const int32_t cpr = a.R >> 3;
+    int nch = 2;
+    bool guard = false;
+    if (cpr % 128 == 0) nch = 2;
+    else if (cpr % 64 == 0) nch = 1;
+    else guard = true;
+    const int32_t per_seq = mode == kPrefix ? a.max_len : a.width;
+    GroupGeom g;
+    g.nseg = (cpr + nch * 64 - 1) / (nch * 64);
+    g.seg_div = make_fastdiv((uint32_t)g.nseg);
+    const int64_t units = (int64_t)a.batch * per_seq * ntens * g.nseg;
+    const bool run = units >= 8192 && units <= 16384;
+    // one tensor per group when the present tensors' formats differ, and for
+    // large contiguous launches (no lookup to share, more waves to spread)
+    const int NT = (fmt < 0 || ntens == 1 || (mode == kContig && units > 16384)) ? 1 : 2;
+    const int P = run ? (NT == 2 ? 4 : 8) : 1;
+    const int64_t tblocks = (per_seq + P - 1) / P;
+    g.inner = (int32_t)(tblocks * g.nseg);
+    g.inner_div = make_fastdiv((uint32_t)g.inner);
+    g.split = (NT == 1 && ntens == 2) ? 1 : 0;
+    g.tens0 = a.k_src ? 0 : 1;
+    g.n_groups = (int32_t)((int64_t)a.batch * (g.split ? 2 : 1) * g.inner);   // bounded by the host checks
+    g.page_div = make_fastdiv(mode == kContig ? 1u : (uint32_t)a.page_size);
+    const void* fn = mode == kPaged    ? widen_fn_mode<kPaged>(fmt, nch, guard, P, NT)
+                     : mode == kPrefix ? widen_fn_mode<kPrefix>(fmt, nch, guard, P, NT)
+                                       : widen_fn_mode<kContig>(fmt, nch, guard, P, NT);
+    // renumbering by XCD pays off for paged runs of one resident generation
+    return launch_groups(fn, g, mode != kContig && run, a, stream);
+}
+
+int launch_quant_kv(const QLaunch& a, void* stream) { return launch_to_compact(a, stream); }
 
 int launch_dequant_kv(const QLaunch& a, void* stream) {
-    return launch_units(a, false, false, a.page_size ? kPaged : kContig, stream);
+    return launch_to_fp16(a, a.page_size ? kPaged : kContig, stream);
 }
 
-int launch_fp16_to_kv(const QLaunch& a, void* stream) {
-    return launch_units(a, true, true, a.page_size ? kPaged : kContig, stream);
-}
+int launch_fp16_to_kv(const QLaunch& a, void* stream) { return launch_to_compact(a, stream); }
 
 int launch_kv_to_fp16(const QLaunch& a, void* stream) {
-    return launch_units(a, false, true, a.page_size ? kPaged : kContig, stream);
+    return launch_to_fp16(a, a.page_size ? kPaged : kContig, stream);
 }
 
-int launch_kv_to_fp16_prefix(const QLaunch& a, void* stream) {
-    return launch_units(a, false, true, kPrefix, stream);
-}
+int launch_kv_to_fp16_prefix(const QLaunch& a, void* stream) { return launch_to_fp16(a, kPrefix, stream); }
+
+// ---------------------------------------------------------------- self-tests
 
 int launch_selftest_codes(const uint16_t* x, int64_t nx, const uint16_t* s, int64_t ns, int wbits,
                           bool force_clamp, uint8_t* u, void* stream) {
@@ -705,6 +999,26 @@ int launch_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, uint32
     dim3 grid((unsigned)((count + kThreads - 1) / kThreads));
     void* args[] = {&n, &count, &f, &q};
     return launch(reinterpret_cast<const void*>(&selftest_fastdiv_kernel), grid, dim3(kThreads), args, stream);
+}
+
+template <int VPL>
+static const void* copy_fn(int wpb) {
+    if (wpb == 1) return reinterpret_cast<const void*>(&selftest_copy_kernel<VPL, 1>);
+    if (wpb == 2) return reinterpret_cast<const void*>(&selftest_copy_kernel<VPL, 2>);
+    if (wpb == 4) return reinterpret_cast<const void*>(&selftest_copy_kernel<VPL, 4>);
+    return reinterpret_cast<const void*>(&selftest_copy_kernel<VPL, 8>);
+}
+
+int launch_selftest_copy(const void* src, void* dst, int64_t n16, int lane_bytes, int group_waves, int64_t max_waves,
+                         void* stream) {
+    const int vpl = lane_bytes / 16;
+    const int64_t tiles = (n16 + vpl * 64 - 1) / (vpl * 64);
+    const int64_t waves = max_waves > 0 && max_waves < tiles ? max_waves : tiles;
+    const dim3 grid((unsigned)((waves + group_waves - 1) / group_waves));
+    void* args[] = {&src, &dst, &n16};
+    const void* fn = vpl == 1 ? copy_fn<1>(group_waves) : vpl == 2 ? copy_fn<2>(group_waves)
+                   : vpl == 4 ? copy_fn<4>(group_waves) : copy_fn<8>(group_waves);
+    return launch(fn, grid, dim3(64 * group_waves), args, stream);
 }
 
 }  // namespace kvq

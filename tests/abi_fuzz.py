@@ -123,14 +123,14 @@ def fuzz_valid(lib, n=5000, seed=8):
                         None, None, 0, wb, None)
             elif which == 2:                                      # paged K/V
                 batch = int(1 << int(rng.integers(0, 15)))
-                cols = max(1, ((1 << 31) - 1) // dim1 // int(rng.integers(1, 4)))
+                cols = max(1, (1 << 30) // dim1 // int(rng.integers(1, 4)))
                 width = int(rng.integers(1, 1 << int(rng.integers(1, 29))))
                 fn = lib.kvq_fp16_to_q_kv if rng.random() < 0.5 else lib.kvq_q_to_fp16_kv
                 rc = fn(_far(1), _far(2), _far(3), _far(4), _far(5), _far(6), shape, batch, 0, width, dim1,
                         _far(7), _far(8), cols, wb, None)
             else:                                                 # full prefix
                 batch = int(1 << int(rng.integers(0, 15)))
-                cols = max(1, ((1 << 31) - 1) // dim1 // int(rng.integers(1, 4)))
+                cols = max(1, (1 << 30) // dim1 // int(rng.integers(1, 4)))
                 max_len = int(rng.integers(1, 1 << int(rng.integers(1, 29))))
                 rc = lib.kvq_kv_to_fp16_prefix(_far(1), _far(2), _far(3), wb, _far(4), _far(5), _far(6), wb,
                                                shape, batch, int(rng.integers(0, 300)), max_len, _far(7), _far(8),

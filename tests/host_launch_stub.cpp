@@ -5,9 +5,10 @@
 //
 // The stand-ins also check what the validation admitted: a launch the real
 // launcher would build with more work-items in a grid dimension than a
-// dispatch's 32-bit grid size holds aborts the process (K/V calls: one
-// 64-lane wavefront per row segment of at least 512 elements; 8-bit calls:
-// one thread per 8 elements at most).
+// dispatch's 32-bit grid size holds aborts the process (K/V calls: at most
+// one 64-lane wavefront per row segment of at least 512 elements, the grid
+// padded to a multiple of 8 workgroups of 4 waves; 8-bit calls: one thread
+// per 8 elements at most).
 #include <stdlib.h>
 
 #include "../kv_cache_quantization_kvq_amd/csrc/kvq_internal.h"
@@ -27,7 +28,8 @@ static int kv_launch(const QLaunch& a, bool prefix) {
     const int64_t tensors = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
     const int64_t segments = (a.R + 511) / 512;
     const int64_t units = mul_or_abort(mul_or_abort(mul_or_abort(a.batch, per_seq), tensors), segments);
-    if (mul_or_abort(units, 64) >= (INT64_C(1) << 32)) abort();
+    const int64_t groups = ((units + 3) / 4 + 7) / 8 * 8;
+    if (mul_or_abort(groups, 256) >= (INT64_C(1) << 32)) abort();
     return no_device();
 }
 
@@ -48,5 +50,9 @@ int launch_selftest_codes(const uint16_t*, int64_t, const uint16_t*, int64_t, in
 }
 int launch_selftest_scales(const uint16_t*, int64_t, int, uint16_t*, void*) { return no_device(); }
 int launch_selftest_fastdiv(const uint32_t*, int64_t, uint32_t, uint32_t*, void*) { return no_device(); }
+int launch_selftest_copy(const void*, void*, int64_t n16, int, int, int64_t, void*) {
+    if (n16 >= (INT64_C(1) << 32)) abort();
+    return no_device();
+}
 
 }  // namespace kvq

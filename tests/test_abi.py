@@ -166,7 +166,7 @@ def test_size_bounds(lib):
     f = lib.kvq_fp16_to_fp8
     assert f(A, A + GB, shp(d0=1, d1=2, h=8193, d=128), 0, 0, 2, None) == SHAPE
     # a launch's work-items must fit 32 bits: batch * width * 2 tensors *
-    # ceil(R / 512) segments is at most 2^26 - 16 (R = 1024: 2 per row)
+    # ceil(R / 512) segments is at most 2^26 - 64 (R = 1024: 2 per row)
     far3 = ((1 << 60), (2 << 60), (3 << 60))
     far6 = ((4 << 60), (5 << 60), (6 << 60))
     s_big = shp(d0=1 << 13, d1=1 << 12, h=8, d=128)
@@ -180,9 +180,16 @@ def test_size_bounds(lib):
     assert f(A, A + GB, big, 0, 0, 2, None) == RANGE
     far = (1 << 60, 2 << 60, 3 << 60)                      # 2^50 elements: 2 PiB of fp16
     assert q(lib, s=shp(d0=1 << 20, d1=1 << 20, h=8, d=128), k=far, v=(None,) * 3, batch=0) == 0
-    # extreme table extents of a call with nothing to do: no overflow, success
-    assert q(lib, s=shp(d0=4, d1=1), page_size=1, sl=A + 6 * GB, bt=A + 7 * GB, cols=(1 << 31) - 1,
+    # extreme table extents of a call with nothing to do: no overflow, success;
+    # a table row addresses at most 2^30 positions (cols * page_size)
+    assert q(lib, s=shp(d0=4, d1=1), page_size=1, sl=A + 6 * GB, bt=A + 7 * GB, cols=1 << 30,
              batch=(1 << 31) - 1, width=0) == 0
+    assert q(lib, s=shp(d0=4, d1=1), page_size=1, sl=A + 6 * GB, bt=A + 7 * GB, cols=(1 << 30) + 1,
+             batch=1, width=0) == RANGE
+    assert q(lib, s=shp(d0=4, d1=2), page_size=2, sl=A + 6 * GB, bt=A + 7 * GB, cols=1 << 29,
+             batch=1, width=0) == 0
+    assert q(lib, s=shp(d0=4, d1=2), page_size=2, sl=A + 6 * GB, bt=A + 7 * GB, cols=(1 << 29) + 1,
+             batch=1, width=0) == RANGE
 
 
 def test_q_zero_work_returns_ok(lib):
