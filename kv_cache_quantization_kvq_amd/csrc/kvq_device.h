@@ -70,10 +70,12 @@ __device__ __forceinline__ uint32_t absmax_2chunks(uint4 v, uint4 w) {
 // ---------------------------------------------------------------- scale
 
 // s16 = fp16_rne(a / Q) computed as fp16_rne(a * fl32(1/Q)).  For every
-// finite fp16 a and Q in {7, 31} this equals the correctly rounded a/Q: the
-// product is within 1.5 ulp32 of a/Q, and a/Q is never that close to an
-// fp16 rounding boundary unless it is exactly representable (checked
-// exhaustively on the device by the self-test hooks).
+// finite fp16 a and Q in {7, 31, 127} (4-, 6- and 8-bit codes) this equals
+// the correctly rounded a/Q: the product is within 1.5 ulp32 of a/Q, and a/Q
+// is never that close to an fp16 rounding boundary unless it is exactly
+// representable.  The GPU test of the scale rule checks all 31,744 finite
+// fp16 absmax values at each of the three widths against the oracle's
+// divide.
 template <int WBITS>
 __device__ __forceinline__ uint32_t scale_from_absmax(uint32_t a_bits) {
     constexpr float kInvQ = 1.0f / (float)((1 << (WBITS - 1)) - 1);

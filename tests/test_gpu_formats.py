@@ -147,8 +147,14 @@ def _paged_rows_check(k, v, kc, ks, vc, vs, ko, vo, fk, fv, rows, what, n_untouc
     for name, src, c, sc, o, fmt in (("K", k, kc, ks, ko, fk), ("V", v, vc, vs, vo, fv)):
         xin = gather_rows(src, valid)
         if fmt == 0:
-            want_c = xin.view(np.uint8).reshape(xin.shape[0], -1)[:, 1::2]
-            want_o = xin & 0xFF00
+            # the oracle's 8-bit conversion of the gathered rows, both ways
+            x4 = xin.reshape(1, xin.shape[0], 1, -1)
+            want_c = np.empty(x4.shape, np.uint8)
+            oracle.fp16_to_fp8(x4, want_c, 1, 0, xin.shape[0])
+            want_o = np.empty(x4.shape, np.float16)
+            oracle.fp8_to_fp16(want_c, want_o, 1, 0, xin.shape[0])
+            want_c = want_c.reshape(xin.shape[0], -1)
+            want_o = want_o.view(np.uint16).reshape(xin.shape[0], -1)
         else:
             want_c, want_s = oracle.quant_rows(xin, fmt)
             byte_diff(gather_rows(sc, valid).view(np.uint16), want_s, what + " %s scales" % name)

@@ -1,0 +1,240 @@
+"""GPU parity of the launch shapes the conversions choose by size, against
+the CPU oracle, byte for byte (every output byte, untouched sentinel bytes
+included).
+
+The kernels pick their work decomposition per launch: rows whose length is
+a multiple of 1024 elements are quantized two row segments per wave through
+an LDS transpose (one 32-element block per lane), other rows one segment
+per wave; launches of 8,192 to 16,384 units are widened in runs of 4
+positions of K and V (8 of one tensor) per wave with workgroups renumbered
+by XCD, other launches one position per wave.  These cases sit on each side
+of those choices, with page sizes that make a run of positions cross pages,
+invalid table entries, positions before the cache and past the table, odd
+window widths (the last pair of a sequence has one live unit), rows of 2048
+and 3072 elements (a pair spans two rows), one tensor only, and K and V at
+different formats.  Operations: ExLlamaV2 cache page, Description of
+fp16_to_q_kv / q_to_fp16_kv (paged and contiguous), plus the per-tensor and
+full-prefix entry points of include/kvq.h.
+
+(The "ExLlamaV2 cache page" in this file is the page "Implementation: Turboderp org
+Exllamav2 Ext Cache".)
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import byte_diff, dev, host, need_lib, sentinel, sentinel_np, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    assert torch().cuda.is_available(), "GPU tests need a ROCm device"
+    return need_lib()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _cshape(shape, fmt):
+    return tuple(shape) if fmt == 0 else (shape[0], shape[1], shape[2], shape[3] * fmt // 8)
+
+
+def _sshape(shape):
+    return (shape[0], shape[1], shape[2], shape[3] // 32)
+
+
+def _data(rng, shape, scale):
+    x = rng.standard_normal(shape, dtype=np.float32) * scale
+    # a few all-zero blocks and tiny values (zero and subnormal scales)
+    flat = x.reshape(-1, 32)
+    pick = rng.random(flat.shape[0])
+    flat[pick < 0.002] = 0
+    flat[(pick >= 0.002) & (pick < 0.004)] *= 1e-6
+    return x.astype(np.float16)
+
+
+def _tables(rng, dim0, batch, cols, ps, width, bad_frac=0.05):
+    bt = rng.permutation(dim0).astype(np.int32)[:batch * cols].reshape(batch, cols).copy()
+    bad = rng.random(bt.shape) < bad_frac
+    bt[bad] = rng.choice(np.array([-1, -9, dim0, dim0 + 7], np.int32), size=int(bad.sum()))
+    sl = rng.integers(-5, cols * ps - width + 6, size=batch).astype(np.int32)
+    return sl, bt
+
+
+def _roundtrip(kvq, k, v, fk, fv, batch, offset, width, ps=0, sl=None, bt=None, what=""):
+    """Per-tensor entry points (K at fk, V at fv; None drops a tensor) both
+    ways, compared with the oracle on every byte."""
+    t = torch()
+    shape = (k if k is not None else v).shape
+    kd = dev(k) if k is not None else None
+    vd = dev(v) if v is not None else None
+    def bufs(f, present):
+        if not present:
+            return None, None, None, None
+        c = sentinel(_cshape(shape, f), t.uint8)
+        s = None if f == 0 else sentinel(_sshape(shape), t.float16)
+        oc = sentinel_np(_cshape(shape, f), np.uint8)
+        os_ = None if f == 0 else sentinel_np(_sshape(shape), np.float16)
+        return c, s, oc, os_
+    kc, ks, okc, oks = bufs(fk, k is not None)
+    vc, vs, ovc, ovs = bufs(fv, v is not None)
+    sld, btd = (dev(sl), dev(bt)) if ps else (None, None)
+    kvq.kvq_fp16_to_kv(kd, kc, ks, fk, vd, vc, vs, fv, batch, offset, width, ps, sld, btd)
+    ko = sentinel(shape, t.float16) if k is not None else None
+    vo = sentinel(shape, t.float16) if v is not None else None
+    kvq.kvq_kv_to_fp16(kc, ko, ks, fk, vc, vo, vs, fv, batch, offset, width, ps, sld, btd)
+    oracle.fp16_to_kv(k, okc, oks, fk, v, ovc, ovs, fv, batch, offset, width, ps, sl, bt)
+    oko = sentinel_np(shape, np.float16) if k is not None else None
+    ovo = sentinel_np(shape, np.float16) if v is not None else None
+    oracle.kv_to_fp16(okc, oko, oks, fk, ovc, ovo, ovs, fv, batch, offset, width, ps, sl, bt)
+    for got, want, name in ((kc, okc, "K compact"), (ks, oks, "K scales"), (ko, oko, "K fp16"),
+                            (vc, ovc, "V compact"), (vs, ovs, "V scales"), (vo, ovo, "V fp16")):
+        if want is None:
+            assert got is None
+            continue
+        byte_diff(host(got), want, "%s %s" % (what, name))
+
+
+@pytest.mark.parametrize("ps", [1, 3, 16])
+@pytest.mark.parametrize("fmt", [4, 6, 8, 0])
+def test_paged_run_size(kvq, ps, fmt):
+    """16 sequences x 256 positions of K and V (8,192 units, rows of 1024):
+    runs of 4 positions cross pages of 1, 3 and 16 tokens."""
+    rng = np.random.default_rng(4000 + 10 * ps + fmt)
+    batch, width = 16, 256
+    cols = (width + 12) // ps + 2
+    dim0 = batch * cols + 5
+    shape = (dim0, ps, 8, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 0.3)
+    sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+    _log("paged run size ps=%d fmt=%d" % (ps, fmt))
+    _roundtrip(kvq, k, v, fmt, fmt, batch, 2, width, ps, sl, bt, what="paged ps=%d fmt=%d" % (ps, fmt))
+
+
+def test_paged_single_width_run_size(kvq):
+    """The page's single-width calls (one wbits for K and V) at the run size,
+    13 sequences x 317 positions: an odd width, 8,242 units, a grid padded
+    to a multiple of 8 workgroups."""
+    t = torch()
+    rng = np.random.default_rng(4100)
+    batch, width, ps = 13, 317, 16
+    cols = (width + 12) // ps + 2
+    dim0 = batch * cols + 3
+    shape = (dim0, ps, 8, 128)
+    k, v = _data(rng, shape, 2.0), _data(rng, shape, 0.05)
+    sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+    for wbits in (4, 6, 8):
+        cs, ss = _cshape(shape, wbits), _sshape(shape)
+        kq, vq = sentinel(cs, t.uint8), sentinel(cs, t.uint8)
+        ks, vs = sentinel(ss, t.float16), sentinel(ss, t.float16)
+        ko, vo = sentinel(shape, t.float16), sentinel(shape, t.float16)
+        kvq.kvq_fp16_to_q_kv(dev(k), kq, ks, dev(v), vq, vs, batch, 0, width, ps, dev(sl), dev(bt), wbits)
+        kvq.kvq_q_to_fp16_kv(kq, ko, ks, vq, vo, vs, batch, 0, width, ps, dev(sl), dev(bt), wbits)
+        okq, ovq = sentinel_np(cs, np.uint8), sentinel_np(cs, np.uint8)
+        oks, ovs = sentinel_np(ss, np.float16), sentinel_np(ss, np.float16)
+        oracle.fp16_to_q_kv(k, okq, oks, v, ovq, ovs, batch, 0, width, ps, sl, bt, wbits)
+        oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+        oracle.q_to_fp16_kv(okq, oko, oks, ovq, ovo, ovs, batch, 0, width, ps, sl, bt, wbits)
+        for got, want, name in ((kq, okq, "K codes"), (vq, ovq, "V codes"), (ks, oks, "K scales"),
+                                (vs, ovs, "V scales"), (ko, oko, "K fp16"), (vo, ovo, "V fp16")):
+            byte_diff(host(got), want, "single width Q%d %s" % (wbits, name))
+
+
+@pytest.mark.parametrize("heads", [16, 24])
+@pytest.mark.parametrize("fmt", [4, 6, 8, 0])
+def test_long_rows(kvq, heads, fmt):
+    """Rows of 2048 and 3072 elements (two or three segments: a pair of
+    units spans two rows when the count is odd), contiguous and paged, at a
+    small size and at the run size."""
+    rng = np.random.default_rng(4200 + heads + fmt)
+    R = heads * 128
+    shape = (6, 48, heads, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 4.0)
+    _log("long rows R=%d fmt=%d contig" % (R, fmt))
+    _roundtrip(kvq, k, v, fmt, fmt, 5, 3, 37, what="contig R=%d fmt=%d" % (R, fmt))
+    # paged at the run size: units = batch * width * 2 * nseg in [8192, 16384]
+    nseg = R // 1024
+    batch, ps = 8, 5
+    width = 8192 // (2 * nseg * batch) + 3
+    cols = (width + 12) // ps + 2
+    dim0 = batch * cols + 2
+    pshape = (dim0, ps, heads, 128)
+    k, v = _data(rng, pshape, 1.0), _data(rng, pshape, 0.5)
+    sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+    _log("long rows R=%d fmt=%d paged run size" % (R, fmt))
+    _roundtrip(kvq, k, v, fmt, fmt, batch, 1, width, ps, sl, bt, what="paged R=%d fmt=%d" % (R, fmt))
+
+
+@pytest.mark.parametrize("fmts", [(4, 6), (6, 4), (0, 8), (8, 0)])
+def test_mixed_formats_run_size(kvq, fmts):
+    """K and V at different formats in one launch at the run size (one
+    tensor per wave, 8 positions, format chosen per wave)."""
+    rng = np.random.default_rng(4300 + 10 * fmts[0] + fmts[1])
+    batch, width, ps = 16, 300, 7
+    cols = (width + 12) // ps + 2
+    dim0 = batch * cols + 1
+    shape = (dim0, ps, 8, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 1.0)
+    sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+    _roundtrip(kvq, k, v, fmts[0], fmts[1], batch, 0, width, ps, sl, bt, what="mixed %s" % (fmts,))
+
+
+@pytest.mark.parametrize("which", ["k", "v"])
+@pytest.mark.parametrize("fmt", [4, 0])
+def test_one_tensor_run_size(kvq, which, fmt):
+    """One tensor only (the other triple absent) at the run size: one tensor
+    per wave, 8 positions per run."""
+    rng = np.random.default_rng(4400 + fmt + (which == "v"))
+    batch, width, ps = 32, 400, 32
+    cols = (width + 12) // ps + 2
+    dim0 = batch * cols + 4
+    shape = (dim0, ps, 8, 128)
+    x = _data(rng, shape, 1.0)
+    sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+    k, v = (x, None) if which == "k" else (None, x)
+    _roundtrip(kvq, k, v, fmt, fmt, batch, 0, width, ps, sl, bt, what="only %s fmt=%d" % (which, fmt))
+
+
+def test_contig_run_size_odd(kvq):
+    """Contiguous windows at the run size with an odd width: 16 x 301
+    positions of K and V (9,632 units)."""
+    rng = np.random.default_rng(4500)
+    shape = (17, 400, 8, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 0.01)
+    for fmt in (4, 6, 8, 0):
+        _roundtrip(kvq, k, v, fmt, fmt, 16, 57, 301, what="contig odd fmt=%d" % fmt)
+
+
+@pytest.mark.parametrize("fmts", [(4, 4), (6, 0)])
+def test_prefix_run_size(kvq, fmts):
+    """Full-prefix widen at the run size: 8 sequences x 1024 positions of K
+    and V (16,384 units), lengths well below the cap so most runs end inside
+    the cache, invalid table entries."""
+    t = torch()
+    fk, fv = fmts
+    rng = np.random.default_rng(4600 + 10 * fk + fv)
+    B, ps, cols = 8, 16, 64
+    num_pages = B * cols + 9
+    shape = (num_pages, ps, 8, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 2.0)
+    bt = rng.permutation(num_pages).astype(np.int32)[:B * cols].reshape(B, cols).copy()
+    bt[rng.random(bt.shape) < 0.03] = -2
+    sl = rng.integers(-3, 990, size=B).astype(np.int32)
+    width, max_len = 7, cols * ps
+    okc = sentinel_np(_cshape(shape, fk), np.uint8)
+    oks = None if fk == 0 else sentinel_np(_sshape(shape), np.float16)
+    ovc = sentinel_np(_cshape(shape, fv), np.uint8)
+    ovs = None if fv == 0 else sentinel_np(_sshape(shape), np.float16)
+    oracle.fp16_to_kv(k, okc, oks, fk, v, ovc, ovs, fv, num_pages, 0, ps)
+    ko, vo = sentinel(shape, t.float16), sentinel(shape, t.float16)
+    _log("prefix run size %s" % (fmts,))
+    kvq.kvq_kv_to_fp16_prefix(dev(okc), ko, None if oks is None else dev(oks), fk,
+                              dev(ovc), vo, None if ovs is None else dev(ovs), fv,
+                              B, width, max_len, dev(sl), dev(bt))
+    oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+    oracle.kv_to_fp16_prefix(okc, oko, oks, fk, ovc, ovo, ovs, fv, B, width, max_len, sl, bt)
+    byte_diff(host(ko), oko.view(np.uint16), "prefix run size K")
+    byte_diff(host(vo), ovo.view(np.uint16), "prefix run size V")

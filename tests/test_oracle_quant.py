@@ -189,7 +189,7 @@ def _round_trip_ok(x_bits, s16, u, xq_bits, wbits):
     if s == 0:
         return bool((xq == 0).all() and (np.abs(x) <= Q * 2.0 ** -25).all())
     q = u.astype(np.int64) - Z
-    clamped = (q == -Z) | (q == Z - 1) & (np.abs(x) > (Z - 0.5) * s)
+    clamped = ((q == -Z) | (q == Z - 1)) & (np.abs(x) > (Z - 0.5) * s)
     ok = np.isinf(xq) | clamped
     ulp = np.zeros_like(xq)
     fin = np.isfinite(xq)                   # infinite x' is accepted above
