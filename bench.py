@@ -465,7 +465,7 @@ def main():
 
 
 # kernel names of the paged-Q4 launches (rocprofv3 spelling)
-KERNEL_NAMES = {"quant": "kvq::narrow_pair_kernel<4, 1>",
+KERNEL_NAMES = {"quant": "kvq::narrow_run_kernel<4, 1, 2>",
                 "dequant": "kvq::widen_run_kernel<4, 1, 2, false, 4, 2>"}
 
 

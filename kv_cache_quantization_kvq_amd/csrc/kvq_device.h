@@ -50,21 +50,38 @@ __device__ __forceinline__ uint32_t pair_max(uint32_t v) {
     return v > o ? v : o;
 }
 
-// Largest |x| of the 16 fp16 values of two chunks, as fp16 bits.  For
-// finite values, ordering of |x| equals unsigned ordering of the bits with
-// the sign cleared, so this is packed u16 max on (bits & 0x7FFF).
-__device__ __forceinline__ uint32_t absmax_2chunks(uint4 v, uint4 w) {
-    u16x2_t m0 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu),
-                                           __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu));
-    u16x2_t m1 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu),
-                                           __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu));
-    u16x2_t m2 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, w.x & 0x7FFF7FFFu),
-                                           __builtin_bit_cast(u16x2_t, w.y & 0x7FFF7FFFu));
-    u16x2_t m3 = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, w.z & 0x7FFF7FFFu),
-                                           __builtin_bit_cast(u16x2_t, w.w & 0x7FFF7FFFu));
-    u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
-                                          __builtin_elementwise_max(m2, m3));
+// Running magnitude maximum per fp16 half: max(acc, w, -w) = max(acc, |w|)
+// in one v_pk_maximum3_f16 (third source negated in both halves).  This is
+// the IEEE 754-2019 maximum, so a zero of either sign gives +0; for finite
+// fp16 (the quantizer's domain; fp16 denormals are kept) the result is the
+// largest magnitude, and such non-negative values order like their bits.
+__device__ __forceinline__ uint32_t absmax_step(uint32_t acc, uint32_t w) {
+    uint32_t d;
+    asm("v_pk_maximum3_f16 %0, %1, %2, %2 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "=v"(d) : "v"(acc), "v"(w));
+    return d;
+}
+
+// Largest |x| of the 2N fp16 values in words w[0..N), N even, as fp16 bits:
+// two interleaved chains of absmax_step, then an integer max of the
+// non-negative halves.
+template <int N>
+__device__ __forceinline__ uint32_t absmax_words(const uint32_t (&w)[N]) {
+    static_assert(N >= 2 && N % 2 == 0, "an even number of words");
+    uint32_t a = absmax_step(w[0], w[0]);
+    uint32_t b = absmax_step(w[1], w[1]);
+#pragma unroll
+    for (int i = 2; i < N; i += 2) {
+        a = absmax_step(a, w[i]);
+        b = absmax_step(b, w[i + 1]);
+    }
+    const u16x2_t m = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b));
     return (uint32_t)(m.x > m.y ? m.x : m.y);
+}
+
+// Largest |x| of the 16 fp16 values of two chunks, as fp16 bits.
+__device__ __forceinline__ uint32_t absmax_2chunks(uint4 v, uint4 w) {
+    const uint32_t x[8] = {v.x, v.y, v.z, v.w, w.x, w.y, w.z, w.w};
+    return absmax_words(x);
 }
 
 // ---------------------------------------------------------------- scale
@@ -214,15 +231,42 @@ __device__ __forceinline__ void quant_chunk(uint4 v, uint32_t s16, const ScaleOp
     else quant_chunk_clamped<WBITS>(v, so, u);
 }
 
-// 4-bit: code j at bits 4j..4j+3 of one little-endian word.  Codes 2..7
-// shift their high garbage past bit 31; codes 0 and 1 are merged through
-// their low byte.
-__device__ __forceinline__ uint32_t pack_q4(const uint32_t (&u)[8]) {
-    uint32_t w = u[2] << 8;
+// The same for N chunks of one block, with one branch for the block.
+template <int WBITS, int N>
+__device__ __forceinline__ void quant_chunks(const uint4 (&v)[N], uint32_t s16, const ScaleOps& so,
+                                             uint32_t (&u)[N][8]) {
+    if (s16 >= 0x0400u) {
 #pragma unroll
-    for (int j = 3; j < 8; ++j) w |= u[j] << (4 * j);
-    const uint32_t t = u[0] | (u[1] << 4);
-    return (t & 0xFFu) | w;
+        for (int k = 0; k < N; ++k) quant_chunk_normal<WBITS>(v[k], so, u[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) quant_chunk_clamped<WBITS>(v[k], so, u[k]);
+    }
+}
+
+// 4-bit: code j at bits 4j..4j+3 of one little-endian word.  Each u[j] is
+// 0x4B000000 + code (the rounding constant's exponent above zero bits
+// 4..23), and the fields do not overlap, so the word is the sum of the u[j]
+// shifted into place (shift-adds, mod 2^32) less the exponent terms that
+// stay inside 32 bits: 0x4B000000 from u[0] and 0xB0000000 from u[1] << 4
+// (those of the higher codes shift out), i.e. plus 0x05000000.
+// (a << SH) + b in one v_lshl_add_u32 (the compiler would otherwise split
+// such chains into shifts and three-input adds).
+template <int SH>
+__device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t b) {
+    uint32_t d;
+    asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "n"(SH), "v"(b));
+    return d;
+}
+
+__device__ __forceinline__ uint32_t pack_q4(const uint32_t (&u)[8]) {
+    const uint32_t t01 = lshl_add<4>(u[1], u[0]);
+    const uint32_t t23 = lshl_add<4>(u[3], u[2]);
+    const uint32_t t45 = lshl_add<4>(u[5], u[4]);
+    const uint32_t t67 = lshl_add<4>(u[7], u[6]);
+    const uint32_t lo = lshl_add<8>(t23, t01);      // exponent terms of u[2], u[3] shift out
+    const uint32_t hi = lshl_add<8>(t67, t45);
+    return lshl_add<16>(hi, lo) + 0x05000000u;      // those of hi shift out
 }
 
 // 6-bit: code j at bits 6j..6j+5 of a 48-bit little-endian field, returned

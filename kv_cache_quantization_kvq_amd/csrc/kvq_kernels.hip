@@ -218,9 +218,11 @@ __device__ __forceinline__ void quant_unit(const QLaunch& a, const UnitRef& ur, 
     load_piece(a, ur, pc, in, x0, x1);
     const uint32_t s16 = scale_from_absmax<WBITS>(pair_max(absmax_2chunks(x0, x1)));
     const ScaleOps so = prep_scale(s16);
-    uint32_t u0[8], u1[8];
-    quant_chunk<WBITS>(x0, s16, so, u0);
-    quant_chunk<WBITS>(x1, s16, so, u1);
+    const uint4 x[2] = {x0, x1};
+    uint32_t u[2][8];
+    quant_chunks<WBITS, 2>(x, s16, so, u);
+    const uint32_t (&u0)[8] = u[0];
+    const uint32_t (&u1)[8] = u[1];
 
     const bool store = ur.live && in;
     uint8_t* codes = static_cast<uint8_t*>(ur.tensor ? a.v_dst : a.k_dst) + ur.row * (int64_t)(R / 8 * WBITS);
@@ -325,31 +327,23 @@ __device__ __forceinline__ bool decode_group(const GroupGeom& g, int32_t& b, int
 
 // ================================================================ fp16 -> compact, block per lane
 //
-// R % 1024 == 0.  A wave converts units u0 = 2k and u1 = 2k + 1 of one
-// (sequence, tensor): unit u is position u / nseg, segment u % nseg (u1 is
-// dead past the last unit).  Instruction i of the load loads chunk
-// c = 64 i + l (16 bytes) of the wave's 4 KB: unit i >> 1, chunk
-// (i & 1) * 64 + l of that unit.  Chunk c goes to LDS slot
-// (c & 3) * 66 + (c >> 2), so lane L later reads its block's chunks
-// 4L .. 4L + 3 from slots j * 66 + L (consecutive lanes, consecutive
-// slots); the stride of 66 keeps the 8 lanes of each write phase in
-// different banks.
+// R % 1024 == 0.  A wave converts units NU k .. NU k + NU - 1 of one
+// (sequence, tensor): unit u is position u / nseg, segment u % nseg (units
+// past the last are dead).  Load instruction i fetches 16 bytes per lane:
+// unit i >> 1, chunk (i & 1) * 64 + l of that unit.  The units are quantized
+// in pairs; within pair q = i >> 2, chunk c = 64 (i & 3) + l goes to slot
+// (c & 3) * 66 + (c >> 2) of the pair's LDS region, so lane L later reads
+// its block's chunks 4L .. 4L + 3 from slots j * 66 + L (consecutive lanes,
+// consecutive slots); the stride of 66 keeps the 8 lanes of each write
+// phase in different banks.  Lanes 0..31 hold the blocks of the pair's
+// first unit, lanes 32..63 those of its second.
 
 constexpr int kLdsSlots = 3 * 66 + 64;   // 16-byte slots per wave
 
 __device__ __forceinline__ uint32_t absmax_block(const uint4 (&v)[4]) {
-    u16x2_t m[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u16x2_t p = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v[i].x & 0x7FFF7FFFu),
-                                                    __builtin_bit_cast(u16x2_t, v[i].y & 0x7FFF7FFFu));
-        const u16x2_t q = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v[i].z & 0x7FFF7FFFu),
-                                                    __builtin_bit_cast(u16x2_t, v[i].w & 0x7FFF7FFFu));
-        m[i] = __builtin_elementwise_max(p, q);
-    }
-    const u16x2_t t = __builtin_elementwise_max(__builtin_elementwise_max(m[0], m[1]),
-                                                __builtin_elementwise_max(m[2], m[3]));
-    return (uint32_t)(t.x > t.y ? t.x : t.y);
+    const uint32_t w[16] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w,
+                            v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
+    return absmax_words(w);
 }
 
 // Codes of the block in v (32 elements, this lane), packed: Q4 in c[0..3],
@@ -360,8 +354,7 @@ __device__ __forceinline__ uint32_t quant_block(const uint4 (&v)[4], uint32_t (&
     const uint32_t s16 = scale_from_absmax<WBITS>(absmax_block(v));
     const ScaleOps so = prep_scale(s16);
     uint32_t u[4][8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) quant_chunk<WBITS>(v[k], s16, so, u[k]);
+    quant_chunks<WBITS, 4>(v, s16, so, u);
     if constexpr (WBITS == 4) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) c[k] = pack_q4(u[k]);
@@ -388,92 +381,102 @@ __device__ __forceinline__ uint32_t quant_block(const uint4 (&v)[4], uint32_t (&
 }
 
 // FMT: 0 (8-bit high byte), 4, 6 or 8 -- the format of the group's tensor.
-template <int FMT, int MODE>
-__device__ __forceinline__ void narrow_pair(const QLaunch& a, const GroupGeom& g, uint4 (*lds)[kLdsSlots],
-                                            bool gok, int32_t b, int32_t tensor, int32_t k) {
+// The wave converts NU (2 or 4) consecutive units of one tensor, loaded
+// together and quantized as NU / 2 pairs; wl is the wave's NU / 2 LDS
+// regions (one per pair).
+template <int FMT, int MODE, int NU>
+__device__ __forceinline__ void narrow_run(const QLaunch& a, const GroupGeom& g, uint4 (*wl)[kLdsSlots],
+                                           bool gok, int32_t b, int32_t tensor, int32_t k) {
+    static_assert(NU == 2 || NU == 4, "two or four units per wave");
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
     const int32_t R = a.R;
     const int32_t units = a.width * g.nseg;
-    int32_t t[2], seg[2];
-    bool in[2];
+    int32_t t[NU], seg[NU], dt[NU];
+    bool in[NU];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int32_t u = 2 * k + h;
+    for (int h = 0; h < NU; ++h) {
+        const int32_t u = NU * k + h;   // unit NU * k is always in range (k < ceil(units / NU))
         in[h] = u < units;
         const int32_t uu = in[h] ? u : units - 1;
         t[h] = (int32_t)fast_div((uint32_t)uu, g.seg_div);
         seg[h] = uu - t[h] * g.nseg;
     }
-    int64_t rr[2], row[2];
-    bool live[2];
-    const int32_t dt[2] = {0, t[1] - t[0]};   // 0 or 1: consecutive units
-    resolve_positions<MODE, 2>(a, g.page_div, b, t[0], dt, in, rr);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NU; ++h) dt[h] = t[h] - t[0];   // in [0, NU): consecutive units
+    int64_t rr[NU], row[NU];
+    bool live[NU];
+    resolve_positions<MODE, NU>(a, g.page_div, b, t[0], dt, in, rr);
+#pragma unroll
+    for (int h = 0; h < NU; ++h) {
         live[h] = gok && rr[h] >= 0;
         row[h] = rr[h] >= 0 ? rr[h] : 0;   // skipped units read row 0 and store nothing
     }
     const uint16_t* src = static_cast<const uint16_t*>(tensor ? a.v_src : a.k_src);
-    uint4 x[4];
+    uint4 x[2 * NU];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2 * NU; ++i)
         x[i] = ld_nt(reinterpret_cast<const uint4*>(src + row[i >> 1] * R + seg[i >> 1] * 1024) + (i & 1) * 64 + lane);
     if constexpr (FMT == 0) {
         uint8_t* dst = static_cast<uint8_t*>(tensor ? a.v_dst : a.k_dst);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2 * NU; ++i) {
             const int h = i >> 1;
             const uint2 d = make_uint2(high_bytes(x[i].x, x[i].y), high_bytes(x[i].z, x[i].w));
             if (live[h]) st_nt(reinterpret_cast<uint2*>(dst + row[h] * R + seg[h] * 1024) + (i & 1) * 64 + lane, d);
         }
     } else {
+        // pair q = i >> 2 holds units 2q, 2q + 1: its chunk c = 64 (i & 3) + l
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = 64 * i + lane;
-            lds[wv][(c & 3) * 66 + (c >> 2)] = x[i];
+        for (int i = 0; i < 2 * NU; ++i) {
+            const int c = 64 * (i & 3) + lane;
+            wl[i >> 2][(c & 3) * 66 + (c >> 2)] = x[i];
         }
         // the wave's own LDS writes are complete before it reads them back
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
-        uint4 v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = lds[wv][j * 66 + lane];
-        const int h = lane >> 5;
-        const int32_t blk = seg[h] * 32 + (lane & 31);
-        uint32_t c[8];
-        const uint32_t s16 = quant_block<FMT>(v, c);
-        constexpr int32_t seg_code_bytes = 128 * FMT;     // a 1024-element segment's codes
+        const bool upper = lane >= 32;        // the lane's block lies in the pair's second unit
         uint8_t* codes = static_cast<uint8_t*>(tensor ? a.v_dst : a.k_dst);
-        uint16_t* scales = static_cast<uint16_t*>(tensor ? a.v_scales : a.k_scales) + row[h] * (int64_t)(R >> 5);
-        if (live[h]) st_nt(scales + blk, s16);
-        if constexpr (FMT == 4) {
-            // 16 bytes per block: consecutive lanes, consecutive blocks
-            if (live[h])
-                st_nt(reinterpret_cast<uint4*>(codes + row[h] * (int64_t)(R / 2)) + blk, make_uint4(c[0], c[1], c[2], c[3]));
-        } else {
-            // 24 or 32 bytes per block: stage the wave's codes (unit 0 then
-            // unit 1, each seg_code_bytes) in its LDS and store them as
-            // contiguous 16-byte lanes
-            uint32_t* cw = reinterpret_cast<uint32_t*>(lds[wv]);
-            constexpr int W = FMT == 8 ? 8 : 6;           // dwords per block
+        constexpr int32_t seg_code_bytes = 128 * FMT;     // a 1024-element segment's codes
 #pragma unroll
-            for (int i = 0; i < W; ++i) cw[lane * W + i] = c[i];
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_wave_barrier();
-            constexpr int pieces = 2 * seg_code_bytes / 16;   // 16-byte pieces of the wave's codes
+        for (int q = 0; q < NU / 2; ++q) {
+            const int h0 = 2 * q, h1 = 2 * q + 1;
+            uint4 v[4];
 #pragma unroll
-            for (int i = 0; i < (pieces + 63) / 64; ++i) {
-                const int pc = 64 * i + lane;
-                if (pc < pieces) {
-                    const uint4 d = lds[wv][pc];
-                    const int uh = pc * 16 >= seg_code_bytes ? 1 : 0;
-                    const int32_t off = pc * 16 - uh * seg_code_bytes;
-                    const bool lv = uh ? live[1] : live[0];
-                    if (lv)
-                        st_nt(reinterpret_cast<uint4*>(codes + (uh ? row[1] : row[0]) * (int64_t)(R / 8 * FMT) +
-                                                       (int64_t)(uh ? seg[1] : seg[0]) * seg_code_bytes + off),
-                              d);
+            for (int j = 0; j < 4; ++j) v[j] = wl[q][j * 66 + lane];
+            const int64_t rowl = upper ? row[h1] : row[h0];
+            const bool livel = upper ? live[h1] : live[h0];
+            const int32_t blk = (upper ? seg[h1] : seg[h0]) * 32 + (lane & 31);
+            uint32_t c[8];
+            const uint32_t s16 = quant_block<FMT>(v, c);
+            uint16_t* scales = static_cast<uint16_t*>(tensor ? a.v_scales : a.k_scales) + rowl * (int64_t)(R >> 5);
+            if (livel) st_nt(scales + blk, s16);
+            if constexpr (FMT == 4) {
+                // 16 bytes per block: consecutive lanes, consecutive blocks
+                if (livel)
+                    st_nt(reinterpret_cast<uint4*>(codes + rowl * (int64_t)(R / 2)) + blk, make_uint4(c[0], c[1], c[2], c[3]));
+            } else {
+                // 24 or 32 bytes per block: stage the pair's codes (unit h0
+                // then unit h1, each seg_code_bytes) in its LDS region and
+                // store them as contiguous 16-byte lanes
+                uint32_t* cw = reinterpret_cast<uint32_t*>(wl[q]);
+                constexpr int W = FMT == 8 ? 8 : 6;           // dwords per block
+#pragma unroll
+                for (int i = 0; i < W; ++i) cw[lane * W + i] = c[i];
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
+                constexpr int pieces = 2 * seg_code_bytes / 16;   // 16-byte pieces of the pair's codes
+#pragma unroll
+                for (int i = 0; i < (pieces + 63) / 64; ++i) {
+                    const int pc = 64 * i + lane;
+                    if (pc < pieces) {
+                        const uint4 d = wl[q][pc];
+                        const bool second = pc * 16 >= seg_code_bytes;
+                        const int32_t off = pc * 16 - (second ? seg_code_bytes : 0);
+                        if (second ? live[h1] : live[h0])
+                            st_nt(reinterpret_cast<uint4*>(codes + (second ? row[h1] : row[h0]) * (int64_t)(R / 8 * FMT) +
+                                                           (int64_t)(second ? seg[h1] : seg[h0]) * seg_code_bytes + off),
+                                  d);
+                    }
                 }
             }
         }
@@ -481,12 +484,12 @@ __device__ __forceinline__ void narrow_pair(const QLaunch& a, const GroupGeom& g
 }
 
 // Every present tensor has format FMT.
-template <int FMT, int MODE>
-__global__ __launch_bounds__(kThreads) void narrow_pair_kernel(QLaunch a, GroupGeom g) {
-    __shared__ uint4 lds[kWaves][kLdsSlots];
+template <int FMT, int MODE, int NU>
+__global__ __launch_bounds__(kThreads) void narrow_run_kernel(QLaunch a, GroupGeom g) {
+    __shared__ uint4 lds[kWaves * (NU / 2)][kLdsSlots];
     int32_t b, tensor, k;
     const bool gok = decode_group(g, b, tensor, k);
-    narrow_pair<FMT, MODE>(a, g, lds, gok, b, tensor, k);
+    narrow_run<FMT, MODE, NU>(a, g, lds + (threadIdx.x >> 6) * (NU / 2), gok, b, tensor, k);
 }
 
 // ================================================================ compact -> fp16, runs of positions
@@ -501,26 +504,33 @@ struct CodeChunk {
     uint32_t s;         // scale (fp16 bits)
 };
 
+// Q6, Q8 and 8-bit take unsigned 32-bit byte offsets from the wave-uniform
+// row base (the scalar-base + vector-offset address form); Q4 keeps signed
+// element offsets (full 64-bit addresses), measured faster for it: paged Q4
+// 8.85 against 9.04 us, while the offset form gave Q6 10.30 against 10.76 us
+// (with the branch-free shift below) and Q8 10.67 against 10.81 us.
 template <int FMT>
 __device__ __forceinline__ CodeChunk load_code_chunk(const uint8_t* __restrict__ codes_row,
-                                                     const uint16_t* __restrict__ scales_row, int32_t c) {
+                                                     const uint16_t* __restrict__ scales_row, uint32_t c) {
     CodeChunk q;
     if constexpr (FMT == 4) {
-        q.lo = ld_nt(reinterpret_cast<const uint32_t*>(codes_row) + c);
+        q.lo = ld_nt(reinterpret_cast<const uint32_t*>(codes_row) + (int32_t)c);
         q.hi = 0;
+        q.s = ld_nt(scales_row + ((int32_t)c >> 2));
+        return q;
     } else if constexpr (FMT == 8 || FMT == 0) {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(codes_row) + 2 * c;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(codes_row + 8u * c);
         q.lo = ld_nt(w);
         q.hi = ld_nt(w + 1);
     } else {
         // chunk c's 6 bytes start at 6c: load the 8 bytes of its 12-byte
         // group that contain them (4-byte aligned); odd chunks are shifted
         // into place after the load.
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(codes_row + 12 * (c >> 1) + 4 * (c & 1));
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(codes_row + (12u * (c >> 1) + 4u * (c & 1)));
         q.lo = ld_nt(w);
         q.hi = ld_nt(w + 1);
     }
-    q.s = FMT == 0 ? 0u : ld_nt(scales_row + (c >> 2));
+    q.s = FMT == 0 ? 0u : ld_nt(reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(scales_row) + 2u * (c >> 2)));
     return q;
 }
 
@@ -529,7 +539,7 @@ __device__ __forceinline__ uint32_t widen_lo(uint32_t w) { return __builtin_amdg
 __device__ __forceinline__ uint32_t widen_hi(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x03040204u); }
 
 template <int FMT>
-__device__ __forceinline__ uint4 convert_chunk(const CodeChunk& q, int32_t c) {
+__device__ __forceinline__ uint4 convert_chunk(const CodeChunk& q, uint32_t c) {
     if constexpr (FMT == 0) {
         return make_uint4(widen_lo(q.lo), widen_hi(q.lo), widen_lo(q.hi), widen_hi(q.hi));
     } else {
@@ -539,14 +549,11 @@ __device__ __forceinline__ uint4 convert_chunk(const CodeChunk& q, int32_t c) {
         } else if constexpr (FMT == 8) {
             return dequant_q8_chunk(q.lo, q.hi, s2);
         } else {
-            uint32_t lo, hi;
-            if (c & 1) {
-                lo = __builtin_amdgcn_alignbit(q.hi, q.lo, 16);
-                hi = q.hi >> 16;
-            } else {
-                lo = q.lo;
-                hi = q.hi & 0xFFFFu;
-            }
+            // an odd chunk's 6 bytes start 2 bytes into the loaded 8: shift
+            // by 16 bits, selected arithmetically (no divergent branch)
+            const uint32_t sh = (c & 1u) << 4;
+            const uint32_t lo = __builtin_amdgcn_alignbit(q.hi, q.lo, sh);
+            const uint32_t hi = __builtin_amdgcn_ubfe(q.hi, sh, 16);
             return dequant_q6_chunk(lo, hi, s2);
         }
     }
@@ -588,8 +595,8 @@ __device__ __forceinline__ void widen_run(const QLaunch& a, const GroupGeom& g, 
                 FMT == 0 ? nullptr : static_cast<const uint16_t*>(tensor ? a.v_scales : a.k_scales) + row * (int64_t)(R >> 5);
 #pragma unroll
             for (int h = 0; h < NCH; ++h) {
-                const int32_t c = seg * (NCH * 64) + h * 64 + lane;
-                if (GUARD) q[p][j][h] = c < cpr ? load_code_chunk<FMT>(codes, scales, c) : CodeChunk{0, 0, 0};
+                const uint32_t c = (uint32_t)(seg * (NCH * 64) + h * 64 + lane);
+                if (GUARD) q[p][j][h] = c < (uint32_t)cpr ? load_code_chunk<FMT>(codes, scales, c) : CodeChunk{0, 0, 0};
                 else q[p][j][h] = load_code_chunk<FMT>(codes, scales, c);
             }
         }
@@ -603,9 +610,9 @@ __device__ __forceinline__ void widen_run(const QLaunch& a, const GroupGeom& g, 
                                                   (rr[p] >= 0 ? rr[p] : 0) * R);
 #pragma unroll
             for (int h = 0; h < NCH; ++h) {
-                const int32_t c = seg * (NCH * 64) + h * 64 + lane;
+                const uint32_t c = (uint32_t)(seg * (NCH * 64) + h * 64 + lane);
                 const uint4 o = convert_chunk<FMT>(q[p][j][h], c);
-                if (rr[p] >= 0 && (!GUARD || c < cpr)) st_nt(dst + c, o);
+                if (rr[p] >= 0 && (!GUARD || c < (uint32_t)cpr)) st_nt(dst + c, o);
             }
         }
     }
@@ -809,16 +816,26 @@ static int launch_groups(const void* fn, GroupGeom& g, bool xcd, QLaunch a, void
 
 // ---------------------------------------------------------------- fp16 -> compact
 
+// Units per wave of the fp16 -> compact run kernel.  Four (two pairs, 8 KB
+// of loads per wave) measured slower at every size tried: paged Q4 10.63
+// against 9.65 us, contiguous 4 x 512 positions 4.43 against 3.94 us.
+constexpr int kNarrowUnits = 2;
+
 template <int MODE>
-static const void* narrow_pair_fn(int fmt) {
+static const void* narrow_run_fn(int fmt) {
     switch (fmt) {
-        case 0: return reinterpret_cast<const void*>(&narrow_pair_kernel<0, MODE>);
-        case 4: return reinterpret_cast<const void*>(&narrow_pair_kernel<4, MODE>);
-        case 6: return reinterpret_cast<const void*>(&narrow_pair_kernel<6, MODE>);
-        case 8: return reinterpret_cast<const void*>(&narrow_pair_kernel<8, MODE>);
+        case 0: return reinterpret_cast<const void*>(&narrow_run_kernel<0, MODE, kNarrowUnits>);
+        case 4: return reinterpret_cast<const void*>(&narrow_run_kernel<4, MODE, kNarrowUnits>);
+        case 6: return reinterpret_cast<const void*>(&narrow_run_kernel<6, MODE, kNarrowUnits>);
+        case 8: return reinterpret_cast<const void*>(&narrow_run_kernel<8, MODE, kNarrowUnits>);
         default: return nullptr;   // no single format: the caller takes the one-unit kernel
     }
 }
+
+// Renumber the run kernel's workgroups by XCD: paged launches of one
+// resident generation (the waves of a sequence then share one L2 for its
+// cache_seqlens and block_table lines).
+static bool narrow_xcd(int64_t total_units, bool paged) { return paged && total_units <= 16384; }
 
 template <int MODE>
 static const void* unit_fn(int fmt, bool guard) {
@@ -837,24 +854,24 @@ static int launch_to_compact(const QLaunch& a, void* stream) {
     const int fmt = common_format(a);
     const int ntens = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
     if (a.R % 1024 == 0 && fmt >= 0) {
-        // pairs of units of one tensor per wave (one format for the launch;
-        // K and V at different widths measured faster one unit per wave:
-        // 18.5 against 19.3 us for K-Q4 + V-Q6 at 64 x 256 positions)
+        // two units of one tensor per wave (one format for the launch; K
+        // and V at different widths measured faster one unit per wave: 18.5
+        // against 19.3 us for K-Q4 + V-Q6 at 64 x 256 positions)
         GroupGeom g;
         g.nseg = a.R / 1024;
         g.seg_div = make_fastdiv((uint32_t)g.nseg);
         const int64_t units = (int64_t)a.width * g.nseg;
-        g.inner = (int32_t)((units + 1) / 2);
+        g.inner = (int32_t)((units + kNarrowUnits - 1) / kNarrowUnits);
         g.inner_div = make_fastdiv((uint32_t)g.inner);
         g.split = ntens == 2 ? 1 : 0;
         g.tens0 = a.k_src ? 0 : 1;
         g.n_groups = (int32_t)((int64_t)a.batch * ntens * g.inner);   // bounded by the host checks
         g.page_div = make_fastdiv(paged ? (uint32_t)a.page_size : 1u);
-        const void* fn = paged ? narrow_pair_fn<kPaged>(fmt) : narrow_pair_fn<kContig>(fmt);
-        // XCD renumbering for launches of one resident generation (at the
-        // paged Q4 size: 9.66 against 9.72 us; at 65,536 contiguous Q6 units
-        // it costs 3%)
-        return launch_groups(fn, g, (int64_t)a.batch * ntens * units <= 16384, a, stream);
+        const void* fn = paged ? narrow_run_fn<kPaged>(fmt) : narrow_run_fn<kContig>(fmt);
+        // XCD renumbering: at the paged Q4 size 9.65 against 9.71 us, for
+        // layer caches with a shared table 9.68 against 9.85 us; contiguous
+        // launches gain nothing (3.94 against 3.88 us for 4 x 512 positions)
+        return launch_groups(fn, g, narrow_xcd((int64_t)a.batch * ntens * units, paged), a, stream);
     }
     // one unit per wave: the row's 16-element pieces, guarded when they are
     // not a multiple of 64
@@ -880,10 +897,12 @@ static int launch_to_compact(const QLaunch& a, void* stream) {
 // Runs of P = 4 positions with both tensors, or P = 8 positions of one
 // tensor, when that makes 1,024 to 2,048 waves (8,192 to 16,384 units): a
 // single resident generation whose waves each keep 8 units in flight, so
-// every lookup finishes before the chip's memory queues fill.  Other
+// every lookup finishes before the chip's memory queues fill.  Other paged
 // launches take one position per wave: small ones to fill the chip, large
 // ones because many short waves stream better over several generations
-// (both tensors of a position in one wave when paged, sharing the lookup).
+// (both tensors of a position in one wave, sharing the lookup).  Contiguous
+// K + V launches up to 16,384 units take 2 positions per wave up to 8,192
+// units and 8 above; larger ones one unit per wave.
 // Measured at the paged Q4 size (16,384 units): 8.97 us for 4 positions x 2
 // tensors per wave with XCD renumbering, against 10.67 us for one position;
 // for the full-prefix widen of the same caches (~530,000 units): 135 us for
@@ -893,8 +912,14 @@ static int launch_to_compact(const QLaunch& a, void* stream) {
 
 template <int FMT, int MODE, int NCH, bool GUARD>
 static const void* widen_fn(int P, int NT) {
-    if (NT == 2) return P == 4 ? reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 4, 2>)
-                               : reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 1, 2>);
+    if (NT == 2) {
+        if constexpr (MODE == kContig) {
+            if (P == 2) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 2, 2>);
+            if (P == 8) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 8, 2>);
+        }
+        return P == 4 ? reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 4, 2>)
+                      : reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 1, 2>);
+    }
     return P == 8 ? reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 8, 1>)
                   : reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 1, 1>);
 }
@@ -936,7 +961,11 @@ static int launch_to_fp16(const QLaunch& a, int mode, void* stream) {
     // one tensor per group when the present tensors' formats differ, and for
     // large contiguous launches (no lookup to share, more waves to spread)
     const int NT = (fmt < 0 || ntens == 1 || (mode == kContig && units > 16384)) ? 1 : 2;
-    const int P = run ? (NT == 2 ? 4 : 8) : 1;
+    int P = run ? (NT == 2 ? 4 : 8) : 1;
+    // contiguous K + V launches up to 16,384 units: 2 positions per wave up
+    // to 8,192 units, 8 above (4 x 512 positions: 3.35 against 4.09 us for
+    // one position; 4 x 2,048 positions: 8.01 against 8.53 us for 4)
+    if (mode == kContig && NT == 2 && units <= 16384) P = units <= 8192 ? 2 : 8;
     const int64_t tblocks = (per_seq + P - 1) / P;
     g.inner = (int32_t)(tblocks * g.nseg);
     g.inner_div = make_fastdiv((uint32_t)g.inner);

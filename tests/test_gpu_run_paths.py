@@ -5,9 +5,11 @@ included).
 The kernels pick their work decomposition per launch: rows whose length is
 a multiple of 1024 elements are quantized two row segments per wave through
 an LDS transpose (one 32-element block per lane), other rows one segment
-per wave; launches of 8,192 to 16,384 units are widened in runs of 4
-positions of K and V (8 of one tensor) per wave with workgroups renumbered
-by XCD, other launches one position per wave.  These cases sit on each side
+per wave; paged launches of 8,192 to 16,384 units are widened in runs of
+4 positions of K and V (8 of one tensor) per wave with workgroups
+renumbered by XCD, other paged launches one position per wave; contiguous
+K + V launches up to 16,384 units in runs of 2 positions (up to 8,192
+units) or 8.  These cases sit on each side
 of those choices, with page sizes that make a run of positions cross pages,
 invalid table entries, positions before the cache and past the table, odd
 window widths (the last pair of a sequence has one live unit), rows of 2048
@@ -238,3 +240,50 @@ def test_prefix_run_size(kvq, fmts):
     oracle.kv_to_fp16_prefix(okc, oko, oks, fk, ovc, ovo, ovs, fv, B, width, max_len, sl, bt)
     byte_diff(host(ko), oko.view(np.uint16), "prefix run size K")
     byte_diff(host(vo), ovo.view(np.uint16), "prefix run size V")
+
+
+@pytest.mark.parametrize("R", [512, 768, 1024])
+def test_contig_small_runs(kvq, R):
+    """Contiguous K + V launches of at most 8,192 units (two positions per
+    wave) with an odd width, rows of one full, one half and one guarded
+    partial segment: 5 x 333 positions."""
+    rng = np.random.default_rng(4700 + R)
+    shape = (6, 400, R // 128, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 3.0)
+    for fmt in (4, 6, 8, 0):
+        _log("contig small runs R=%d fmt=%d" % (R, fmt))
+        _roundtrip(kvq, k, v, fmt, fmt, 5, 41, 333, what="contig small R=%d fmt=%d" % (R, fmt))
+
+
+def _absmax_blocks(rng):
+    """One 32-element block per finite fp16 magnitude m (0 .. 65504): one
+    element is +-m at a random position, the others random magnitudes up to
+    m with random signs; then blocks of -0 only and of mixed zeros."""
+    m = np.arange(0x7C00, dtype=np.uint16)
+    others = (rng.random((m.size, 32)) * (m[:, None].astype(np.float64) + 1)).astype(np.uint16)
+    others = np.minimum(others, m[:, None])
+    pos = rng.integers(0, 32, size=m.size)
+    others[np.arange(m.size), pos] = m
+    sign = (rng.random(others.shape) < 0.5).astype(np.uint16) << 15
+    blocks = others | sign
+    neg_zero = np.full((4, 32), 0x8000, np.uint16)
+    mixed_zero = ((rng.random((4, 32)) < 0.5).astype(np.uint16) << 15)
+    return np.concatenate([blocks, neg_zero, mixed_zero]).view(np.float16)
+
+
+@pytest.mark.parametrize("R", [1024, 1056])
+def test_block_absmax_every_magnitude(kvq, R):
+    """The block maximum of |x| (scale and codes) for every finite fp16
+    magnitude as the block's largest element, either sign, plus blocks of
+    negative and mixed zeros, through the two-unit kernel (rows of 1024)
+    and the one-unit kernel (rows of 1056, guarded), Q4 / Q6 / Q8."""
+    rng = np.random.default_rng(4800 + R)
+    blocks = _absmax_blocks(rng)
+    per_row = R // 32
+    rows = -(-blocks.shape[0] // per_row)
+    flat = np.zeros((rows * per_row, 32), np.float16)
+    flat[:blocks.shape[0]] = blocks
+    x = flat.reshape(1, rows, R // 32, 32)
+    for fmt in (4, 6, 8):
+        _log("block absmax R=%d fmt=%d" % (R, fmt))
+        _roundtrip(kvq, x, None, fmt, fmt, 1, 0, rows, what="absmax R=%d Q%d" % (R, fmt))
