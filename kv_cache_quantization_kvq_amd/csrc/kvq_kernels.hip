@@ -15,13 +15,16 @@
 //     per pair of units of one tensor.  The wave reads its 4 KB of fp16 with
 //     contiguous 16-byte lanes, passes it through LDS, and lane L then owns
 //     32-element block L (unit L / 32): the absmax, scale and codes of a
-//     block are one lane's work, and each lane stores its block's codes with
-//     one 16/24/32-byte store.  8-bit narrowing needs no transpose.
+//     block are one lane's work.  Q4 codes (16 bytes per block) are stored
+//     straight from the lane; Q6 / Q8 codes are restaged through LDS so
+//     every store is 16 contiguous bytes per lane.  8-bit narrowing needs no
+//     transpose.
 //   fp16 -> compact, other R: one wavefront per unit, lane l holding 16
 //     consecutive elements (a block is a lane pair).
 //   compact -> fp16 (dequantize, 8-bit widen, full-prefix widen): one
-//     wavefront per run of P consecutive positions of one sequence, both
-//     tensors (or one tensor when K and V formats differ).  Every load of
+//     wavefront per run of P consecutive positions of one sequence (P = 1,
+//     2, 4 or 8 by launch size), both tensors (or one tensor when K and V
+//     formats differ, or for large contiguous launches).  Every load of
 //     the wave is issued before its first store; lane l converts chunks
 //     (8 elements) l and l + 64 of each unit, so every 128-bit store of the
 //     wave is contiguous.
@@ -817,8 +820,10 @@ static int launch_groups(const void* fn, GroupGeom& g, bool xcd, QLaunch a, void
 // ---------------------------------------------------------------- fp16 -> compact
 
 // Units per wave of the fp16 -> compact run kernel.  Four (two pairs, 8 KB
-// of loads per wave) measured slower at every size tried: paged Q4 10.63
-// against 9.65 us, contiguous 4 x 512 positions 4.43 against 3.94 us.
+// of loads per wave) measured slower at every size tried, also with each
+// pair converted while the next pair's loads were in flight: paged Q4 10.64
+// against 9.53 us, paged 8-bit 11.31 against 10.63 us, contiguous 4 x 512
+// positions 4.24 against 3.78 us.
 constexpr int kNarrowUnits = 2;
 
 template <int MODE>

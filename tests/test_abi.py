@@ -154,6 +154,29 @@ def test_selftest_fastdiv_validation(lib):
     assert f(A, 0, 7, A + GB, None) == 0
 
 
+def test_selftest_copy_validation(lib):
+    """The bandwidth-reference copy rejects every bad argument before any
+    launch; zero bytes return without one."""
+    f = lib.kvq_selftest_copy
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int64, ctypes.c_void_p]
+    assert f(None, A + GB, 1024, 16, 1, 0, None) == NULL
+    assert f(A, None, 1024, 16, 1, 0, None) == NULL
+    assert f(A, A + GB, -16, 16, 1, 0, None) == RANGE
+    assert f(A, A + GB, 1000, 16, 1, 0, None) == RANGE          # not a multiple of 16
+    assert f(A, A + GB, 1024, 16, 1, -1, None) == RANGE
+    for lb in (0, 8, 48, 256):
+        assert f(A, A + GB, 1024, lb, 1, 0, None) == RANGE
+    for gw in (0, 3, 16):
+        assert f(A, A + GB, 1024, 16, gw, 0, None) == RANGE
+    assert f(A + 8, A + GB, 1024, 16, 1, 0, None) == ALIGN
+    assert f(A, A + GB + 4, 1024, 16, 1, 0, None) == ALIGN
+    assert f(A, A + 512, 1024, 16, 1, 0, None) == OVERLAP
+    assert f(A, A, 1024, 16, 1, 0, None) == OVERLAP
+    assert f(A, A + GB, 0, 16, 1, 0, None) == 0
+
+
 def test_size_bounds(lib):
     """Rows up to 2^20 elements are accepted, longer ones are SHAPE; a call
     whose work units exceed the 32-bit numbering is RANGE (checked before any

@@ -57,6 +57,23 @@ def test_scale_rule_exhaustive(kvq, wbits):
     byte_diff(host(out).view(np.uint16), oracle.scale_from_absmax(a, wbits), "scales")
 
 
+def test_selftest_short_output_rejected(kvq):
+    """The self-test hooks reject an output shorter than their input in the
+    binding, before any launch: the output and the bytes after it keep
+    their sentinel."""
+    t = torch()
+    a = dev(np.arange(0x3C00, 0x3C00 + 64, dtype=np.uint16))
+    buf = t.full((128,), 0x5A5A, dtype=t.int16, device="cuda")
+    with pytest.raises(ValueError):
+        kvq.kvq_selftest_scales(a, 4, buf[:63])
+    n = t.arange(64, dtype=t.int32, device="cuda")
+    ibuf = t.full((128,), 0x5A5A5A5A, dtype=t.int32, device="cuda")
+    with pytest.raises(ValueError):
+        kvq.kvq_selftest_fastdiv(n, 7, ibuf[:63])
+    t.cuda.synchronize()
+    assert bool((buf == 0x5A5A).all()) and bool((ibuf == 0x5A5A5A5A).all())
+
+
 @pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_code_rule_exhaustive(kvq, wbits):
     """Device element code on every finite fp16 x under every finite fp16
