@@ -594,6 +594,26 @@ def secondary_workloads(torch, kvq, synth, wl):
     out["paged_q4_layers_shared_table"] = {k: {"us": round(v * 1e6, 2), "GB/s": round(wl.bytes_per_launch / v / 1e9, 1)}
                                            for k, v in kt.items()}
     del layers
+    # the same Q4 conversions at other batch sizes (8 to 128 sequences x 256
+    # new tokens over the same 4096-page caches, 32 rotated seeded paging
+    # draws each): the launch's fixed costs against its size
+    sweep = {}
+    for nb_seq in (8, 16, 64, 128):
+        srng = np.random.default_rng(9300 + nb_seq)
+        tabs = [tuple(t.from_numpy(a).cuda() for a in synth.paging(srng, nb_seq, 32, 4096, 7936))
+                for _ in range(DRAWS)]
+        qa = lambda d, tabs=tabs, n=nb_seq: kvq.kvq_fp16_to_q_kv(wl.k, wl.kq, wl.ks, wl.v, wl.vq, wl.vs, n, 0,
+                                                                 w.width, w.page_size, *tabs[d], 4)
+        da = lambda d, tabs=tabs, n=nb_seq: kvq.kvq_q_to_fp16_kv(wl.kq, wl.ko, wl.ks, wl.vq, wl.vo, wl.vs, n, 0,
+                                                                 w.width, w.page_size, *tabs[d], 4)
+        for d in range(DRAWS):
+            qa(d)
+        kt = time_kernels(t, [("quant", qa, list(range(DRAWS))), ("dequant", da, list(range(DRAWS)))], 4 * DRAWS)
+        nbytes = 2 * nb_seq * w.width * q_row_bytes(4)
+        sweep["batch_%d" % nb_seq] = {k: {"us": round(v * 1e6, 2), "GB/s": round(nbytes / v / 1e9, 1)}
+                                      for k, v in kt.items()}
+        sweep["batch_%d" % nb_seq]["MB"] = round(nbytes / 1e6, 2)
+    out["paged_q4_batch_sweep"] = sweep
     # other block widths on the paged workload
     for wb in (6, 8):
         other = PagedKV(torch, kvq, synth, wbits=wb, share=wl)

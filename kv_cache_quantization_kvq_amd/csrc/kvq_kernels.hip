@@ -837,10 +837,10 @@ static const void* narrow_run_fn(int fmt) {
     }
 }
 
-// Renumber the run kernel's workgroups by XCD: paged launches of one
-// resident generation (the waves of a sequence then share one L2 for its
-// cache_seqlens and block_table lines).
-static bool narrow_xcd(int64_t total_units, bool paged) { return paged && total_units <= 16384; }
+// Renumber the run kernel's workgroups by XCD for paged launches (the waves
+// of a sequence then share one L2 for its cache_seqlens and block_table
+// lines).
+static bool narrow_xcd(bool paged) { return paged; }
 
 template <int MODE>
 static const void* unit_fn(int fmt, bool guard) {
@@ -874,9 +874,11 @@ static int launch_to_compact(const QLaunch& a, void* stream) {
         g.page_div = make_fastdiv(paged ? (uint32_t)a.page_size : 1u);
         const void* fn = paged ? narrow_run_fn<kPaged>(fmt) : narrow_run_fn<kContig>(fmt);
         // XCD renumbering: at the paged Q4 size 9.65 against 9.71 us, for
-        // layer caches with a shared table 9.68 against 9.85 us; contiguous
-        // launches gain nothing (3.94 against 3.88 us for 4 x 512 positions)
-        return launch_groups(fn, g, narrow_xcd((int64_t)a.batch * ntens * units, paged), a, stream);
+        // layer caches with a shared table 9.68 against 9.85 us, 128 x 256
+        // positions 31.9 against 33.1 us; contiguous launches lose (3.94
+        // against 3.88 us for 4 x 512 positions, 33.3 against 31.9 us for
+        // 8 x 4096 positions of Q6)
+        return launch_groups(fn, g, narrow_xcd(paged), a, stream);
     }
     // one unit per wave: the row's 16-element pieces, guarded when they are
     // not a multiple of 64
@@ -899,17 +901,19 @@ static int launch_to_compact(const QLaunch& a, void* stream) {
 
 // ---------------------------------------------------------------- compact -> fp16
 //
-// Runs of P = 4 positions with both tensors, or P = 8 positions of one
-// tensor, when that makes 1,024 to 2,048 waves (8,192 to 16,384 units): a
-// single resident generation whose waves each keep 8 units in flight, so
-// every lookup finishes before the chip's memory queues fill.  Other paged
-// launches take one position per wave: small ones to fill the chip, large
-// ones because many short waves stream better over several generations
-// (both tensors of a position in one wave, sharing the lookup).  Contiguous
-// K + V launches up to 16,384 units take 2 positions per wave up to 8,192
-// units and 8 above; larger ones one unit per wave.
+// Paged launches of 8,192 to 32,768 units run P = 4 positions with both
+// tensors, or P = 8 positions of one tensor, per wave (1,024 to 4,096
+// waves): a single resident generation whose waves each keep 8 units in
+// flight, so every lookup finishes before the chip's memory queues fill.
+// Other paged launches take one position per wave: small ones to fill the
+// chip, large ones because many short waves stream better over several
+// generations (both tensors of a position in one wave, sharing the lookup).
+// Full-prefix launches run 4 positions at 8,192 to 16,384 units.
+// Contiguous K + V launches up to 16,384 units take 2 positions per wave up
+// to 8,192 units and 8 above; larger ones one unit per wave.
 // Measured at the paged Q4 size (16,384 units): 8.97 us for 4 positions x 2
 // tensors per wave with XCD renumbering, against 10.67 us for one position;
+// at 32,768 units 18.4 against 19.2 us, at 65,536 units 35.8 against 35.1;
 // for the full-prefix widen of the same caches (~530,000 units): 135 us for
 // one position x 2 tensors, 148 us for 4 positions, 158 us with XCD
 // renumbering; contiguous Q6 at 65,536 units: 32.1 us for one unit per wave,
@@ -962,10 +966,13 @@ static int launch_to_fp16(const QLaunch& a, int mode, void* stream) {
     g.nseg = (cpr + nch * 64 - 1) / (nch * 64);
     g.seg_div = make_fastdiv((uint32_t)g.nseg);
     const int64_t units = (int64_t)a.batch * per_seq * ntens * g.nseg;
-    const bool run = units >= 8192 && units <= 16384;
     // one tensor per group when the present tensors' formats differ, and for
     // large contiguous launches (no lookup to share, more waves to spread)
     const int NT = (fmt < 0 || ntens == 1 || (mode == kContig && units > 16384)) ? 1 : 2;
+    // paged K + V runs up to 32,768 units still fit one resident generation
+    // (one-tensor runs of 8 positions measured slower there: 20.9 against
+    // 19.3 us for K-Q4 + V-Q6 at 64 x 256 positions)
+    const bool run = units >= 8192 && units <= (mode == kPaged && NT == 2 ? 32768 : 16384);
     int P = run ? (NT == 2 ? 4 : 8) : 1;
     // contiguous K + V launches up to 16,384 units: 2 positions per wave up
     // to 8,192 units, 8 above (4 x 512 positions: 3.35 against 4.09 us for
@@ -981,8 +988,11 @@ static int launch_to_fp16(const QLaunch& a, int mode, void* stream) {
     const void* fn = mode == kPaged    ? widen_fn_mode<kPaged>(fmt, nch, guard, P, NT)
                      : mode == kPrefix ? widen_fn_mode<kPrefix>(fmt, nch, guard, P, NT)
                                        : widen_fn_mode<kContig>(fmt, nch, guard, P, NT);
-    // renumbering by XCD pays off for paged runs of one resident generation
-    return launch_groups(fn, g, mode != kContig && run, a, stream);
+    // renumbering by XCD pays off for every paged launch (128 x 256
+    // positions, one position per wave: 34.4 against 35.1 us) and for
+    // full-prefix runs, not for the one-position full-prefix launches
+    // (155 against 131 us) whose dead waves it gathers
+    return launch_groups(fn, g, mode == kPaged || (mode == kPrefix && run), a, stream);
 }
 
 int launch_quant_kv(const QLaunch& a, void* stream) { return launch_to_compact(a, stream); }

@@ -287,3 +287,21 @@ def test_block_absmax_every_magnitude(kvq, R):
     for fmt in (4, 6, 8):
         _log("block absmax R=%d fmt=%d" % (R, fmt))
         _roundtrip(kvq, x, None, fmt, fmt, 1, 0, rows, what="absmax R=%d Q%d" % (R, fmt))
+
+
+@pytest.mark.parametrize("batch", [48, 70])
+@pytest.mark.parametrize("fmt", [4, 6, 0])
+def test_paged_large_launches(kvq, batch, fmt):
+    """Paged K + V launches past 16,384 units: 48 x 300 positions (28,800
+    units, still runs of 4 positions per wave) and 70 x 300 (42,000 units,
+    one position per wave), both with workgroups renumbered by XCD over a
+    grid padded to a multiple of 8; pages of 16 tokens, invalid entries."""
+    rng = np.random.default_rng(4900 + batch + fmt)
+    width, ps = 300, 16
+    cols = (width + 12) // ps + 2
+    dim0 = batch * cols + 3
+    shape = (dim0, ps, 8, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 0.7)
+    sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+    _log("paged large launch batch=%d fmt=%d" % (batch, fmt))
+    _roundtrip(kvq, k, v, fmt, fmt, batch, 1, width, ps, sl, bt, what="paged large b=%d fmt=%d" % (batch, fmt))
