@@ -497,6 +497,26 @@ def copy_floor(torch, kvq, launch_bytes):
     out["best"] = dict(best[1])
     assert torch.equal(dst[DRAWS - 1], src[DRAWS - 1]), "copy floor: copy mismatch"
     del src, dst
+    # the same bytes per launch in the conversions' uneven shapes: each lane
+    # reads lane_elems 16-byte elements per element it writes (gather, like
+    # quantize: 3.6 bytes read per byte written) or the reverse (scatter,
+    # like dequantize)
+    out["uneven"] = []
+    for gather in (True, False):
+        for lane_elems in (2, 4, 8):
+            light = 2 * nbytes // (lane_elems + 1) // 1024 * 1024
+            heavy = light * lane_elems
+            src = torch.empty((DRAWS, heavy if gather else light), dtype=torch.uint8, device="cuda")
+            dst = torch.empty((DRAWS, light if gather else heavy), dtype=torch.uint8, device="cuda")
+            src.fill_(1)
+            for group_waves in (1, 4):
+                fn = (lambda d, le=lane_elems, gw=group_waves: kvq.kvq_selftest_stream(src[d], dst[d], le, gw))
+                t = time_kernels(torch, [("stream", fn, list(range(DRAWS)))], 4 * DRAWS)["stream"]
+                out["uneven"].append({"shape": "%s %d:1" % ("read:write" if gather else "write:read", lane_elems),
+                                      "lane_elems": lane_elems, "group_waves": group_waves,
+                                      "bytes_moved": heavy + light, "us": round(t * 1e6, 3),
+                                      "GB/s": round((heavy + light) / t / 1e9, 1)})
+            del src, dst
     return out
 
 

@@ -71,6 +71,27 @@ KVQ_API int kvq_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, u
 KVQ_API int kvq_selftest_copy(const void* src, void* dst, int64_t bytes, int lane_bytes, int group_waves,
                               int64_t max_waves, void* hip_stream);
 
+/*
+ * Bandwidth reference for uneven traffic, the shapes of the conversions
+ * (quantize reads about 3.6 bytes per byte written, dequantize the
+ * reverse): per tile of 64 lanes x 16 bytes on the light side, each lane
+ * reads (gather) or writes (scatter) lane_elems 16-byte elements on the
+ * heavy side.  Gather: src_bytes == lane_elems * dst_bytes, and light
+ * element i of dst is the XOR of src elements (i / 64) * 64 * lane_elems +
+ * 64 k + i % 64, k < lane_elems.  Scatter: dst_bytes == lane_elems *
+ * src_bytes, and those dst elements all equal src element i.  All loads
+ * and stores are non-temporal; one wave per tile, group_waves per
+ * workgroup.
+ *   src, dst      device, 16-byte aligned, non-overlapping
+ *   light side    a multiple of 1024 bytes; both sizes below 2^56
+ *   lane_elems    2, 4 or 8;  group_waves 1, 2, 4 or 8
+ * KVQ_ERR_RANGE (sizes not in one of the two ratios, or out of range) /
+ * _ALIGN / _OVERLAP / _NULL before anything is enqueued; zero sizes launch
+ * nothing.
+ */
+KVQ_API int kvq_selftest_stream(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
+                                int lane_elems, int group_waves, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ from . import _build
 
 __all__ = ["KvqError", "kvq_fp16_to_fp8", "kvq_fp8_to_fp16", "kvq_fp16_to_q_kv",
            "kvq_q_to_fp16_kv", "kvq_count_match", "kvq_strerror", "kvq_version",
-           "kvq_selftest_codes", "kvq_selftest_scales", "kvq_selftest_fastdiv", "kvq_selftest_copy", "library_path", "load_library",
+           "kvq_selftest_codes", "kvq_selftest_scales", "kvq_selftest_fastdiv", "kvq_selftest_copy", "kvq_selftest_stream", "library_path", "load_library",
            "code_shape", "scale_shape", "kvq_fp16_to_kv", "kvq_kv_to_fp16", "kvq_kv_to_fp16_prefix",
            "kvq_bytes_per_token", "compact_shape", "KVQ_FMT_FP8", "KVQ_FMT_Q4", "KVQ_FMT_Q6",
            "KVQ_FMT_Q8", "KVQ_FMT_FP16"]
@@ -86,6 +86,7 @@ def load_library():
             "kvq_selftest_scales": (_i, [_vp, _i64, _i, _vp, _vp]),
             "kvq_selftest_fastdiv": (_i, [_vp, _i64, ctypes.c_uint32, _vp, _vp]),
             "kvq_selftest_copy": (_i, [_vp, _vp, _i64, _i, _i, _i64, _vp]),
+            "kvq_selftest_stream": (_i, [_vp, _i64, _vp, _i64, _i, _i, _vp]),
             "kvq_fp16_to_kv": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, Shape, _i, _i, _i, _i,
                                     _vp, _vp, _i, _vp]),
             "kvq_kv_to_fp16": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, Shape, _i, _i, _i, _i,
@@ -478,3 +479,18 @@ def kvq_selftest_copy(src, dst, lane_bytes=16, group_waves=1, max_waves=0, strea
     rc = load_library().kvq_selftest_copy(ps, pd, src.numel(), int(lane_bytes), int(group_waves),
                                           int(max_waves), _stream_handle(stream, dev))
     _check(rc, "kvq_selftest_copy")
+
+
+def kvq_selftest_stream(src, dst, lane_elems=4, group_waves=1, stream=None):
+    """Uneven-traffic bandwidth reference (device uint8 tensors): gather
+    when src holds lane_elems times the bytes of dst (each 16-byte element
+    of dst the XOR of lane_elems elements of src), scatter when dst holds
+    lane_elems times the bytes of src (each element of src written
+    lane_elems times)."""
+    torch = _torch()
+    dev = _device_of(src)
+    ps = _dev_ptr(src, "src", torch.uint8)
+    pd = _dev_ptr(dst, "dst", torch.uint8, dev)
+    rc = load_library().kvq_selftest_stream(ps, src.numel(), pd, dst.numel(), int(lane_elems), int(group_waves),
+                                            _stream_handle(stream, dev))
+    _check(rc, "kvq_selftest_stream")

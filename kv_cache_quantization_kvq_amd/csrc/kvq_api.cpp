@@ -372,4 +372,26 @@ int kvq_selftest_copy(const void* src, void* dst, int64_t bytes, int lane_bytes,
                ? KVQ_ERR_HIP : KVQ_OK;
 }
 
+int kvq_selftest_stream(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes, int lane_elems,
+                        int group_waves, void* hip_stream) {
+    if (!src || !dst) return KVQ_ERR_NULL;
+    if (lane_elems != 2 && lane_elems != 4 && lane_elems != 8) return KVQ_ERR_RANGE;
+    if (group_waves != 1 && group_waves != 2 && group_waves != 4 && group_waves != 8) return KVQ_ERR_RANGE;
+    // sizes below 2^56, so the products below cannot overflow
+    if (src_bytes < 0 || dst_bytes < 0 || src_bytes >= (INT64_C(1) << 56) || dst_bytes >= (INT64_C(1) << 56))
+        return KVQ_ERR_RANGE;
+    const bool gather = src_bytes == dst_bytes * lane_elems;
+    const bool scatter = dst_bytes == src_bytes * lane_elems;
+    if (!gather && !scatter) return KVQ_ERR_RANGE;
+    const int64_t light = gather ? dst_bytes : src_bytes;
+    if (light % 1024 != 0) return KVQ_ERR_RANGE;                 // whole 64-lane tiles of 16 bytes
+    if (!aligned(src, 16) || !aligned(dst, 16)) return KVQ_ERR_ALIGN;
+    const Extent ext[2] = {{src, src_bytes, false}, {dst, dst_bytes, true}};
+    if (any_output_overlap(ext, 2)) return KVQ_ERR_OVERLAP;
+    if (light / 16 > kMaxWorkItems) return KVQ_ERR_RANGE;       // one work-item per light-side element
+    if (light == 0) return KVQ_OK;
+    return kvq::launch_selftest_stream(src, dst, light / 1024, lane_elems, group_waves, gather, hip_stream)
+               ? KVQ_ERR_HIP : KVQ_OK;
+}
+
 }  // extern "C"

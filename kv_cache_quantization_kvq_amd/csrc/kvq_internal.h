@@ -76,5 +76,10 @@ int launch_selftest_fastdiv(const uint32_t* n, int64_t count, uint32_t d, uint32
 // Plain non-temporal copy of n16 16-byte elements (bandwidth reference).
 int launch_selftest_copy(const void* src, void* dst, int64_t n16, int lane_bytes, int group_waves, int64_t max_waves,
                          void* stream);
+// Uneven-traffic reference: `tiles` tiles of 64 lanes, lane_elems 16-byte
+// elements per lane on the heavy side (read when gathering, written when
+// scattering), one on the light side.
+int launch_selftest_stream(const void* src, void* dst, int64_t tiles, int lane_elems, int group_waves, bool gather,
+                           void* stream);
 
 }  // namespace kvq

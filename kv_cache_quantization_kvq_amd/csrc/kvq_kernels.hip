@@ -758,6 +758,39 @@ __global__ __launch_bounds__(64 * WPB) void selftest_copy_kernel(const uint4* __
     }
 }
 
+// Uneven-traffic bandwidth references: per 64-lane tile each lane reads
+// (GATHER) or writes (scatter) VPL 16-byte elements on the tile's heavy side
+// and one element on its light side (the XOR of the elements read, or the
+// element read written VPL times).  Heavy element k of lane l in tile w is
+// w * 64 VPL + 64 k + l; its light element is w * 64 + l.
+template <int VPL, int WPB, bool GATHER>
+__global__ __launch_bounds__(64 * WPB) void selftest_stream_kernel(const uint4* __restrict__ src,
+                                                                   uint4* __restrict__ dst, int64_t tiles) {
+    const int64_t w = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
+    if (w >= tiles) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t heavy = w * (VPL * 64) + lane;
+    const int64_t light = w * 64 + lane;
+    if constexpr (GATHER) {
+        uint4 v[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) v[k] = ld_nt(src + heavy + 64 * k);
+        uint4 acc = v[0];
+#pragma unroll
+        for (int k = 1; k < VPL; ++k) {
+            acc.x ^= v[k].x;
+            acc.y ^= v[k].y;
+            acc.z ^= v[k].z;
+            acc.w ^= v[k].w;
+        }
+        st_nt(dst + light, acc);
+    } else {
+        const uint4 x = ld_nt(src + light);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) st_nt(dst + heavy + 64 * k, x);
+    }
+}
+
 // ================================================================ launchers
 
 static int launch(const void* fn, dim3 grid, dim3 block, void** args, void* stream) {
@@ -921,16 +954,17 @@ static int launch_to_compact(const QLaunch& a, void* stream) {
 
 template <int FMT, int MODE, int NCH, bool GUARD>
 static const void* widen_fn(int P, int NT) {
-    if (NT == 2) {
-        if constexpr (MODE == kContig) {
-            if (P == 2) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 2, 2>);
-            if (P == 8) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 8, 2>);
-        }
-        return P == 4 ? reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 4, 2>)
-                      : reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 1, 2>);
+    // the (P, NT) shapes the launcher picks; any other gets no kernel (the
+    // launch then fails) rather than one whose grid would not match
+    if (NT == 1 && P == 1) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 1, 1>);
+    if (NT == 1 && P == 8) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 8, 1>);
+    if (NT == 2 && P == 1) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 1, 2>);
+    if (NT == 2 && P == 4) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 4, 2>);
+    if constexpr (MODE == kContig) {
+        if (NT == 2 && P == 2) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 2, 2>);
+        if (NT == 2 && P == 8) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 8, 2>);
     }
-    return P == 8 ? reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 8, 1>)
-                  : reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 1, 1>);
+    return nullptr;
 }
 
 template <int MODE, int NCH, bool GUARD>
@@ -941,8 +975,9 @@ static const void* widen_fn_fmt(int fmt, int P, int NT) {
         case 6: return widen_fn<6, MODE, NCH, GUARD>(P, NT);
         case 8: return widen_fn<8, MODE, NCH, GUARD>(P, NT);
         default:   // per-tensor formats: one tensor per group
-            return P == 8 ? reinterpret_cast<const void*>(&widen_run_kernel<-1, MODE, NCH, GUARD, 8, 1>)
-                          : reinterpret_cast<const void*>(&widen_run_kernel<-1, MODE, NCH, GUARD, 1, 1>);
+            if (NT == 1 && P == 1) return reinterpret_cast<const void*>(&widen_run_kernel<-1, MODE, NCH, GUARD, 1, 1>);
+            if (NT == 1 && P == 8) return reinterpret_cast<const void*>(&widen_run_kernel<-1, MODE, NCH, GUARD, 8, 1>);
+            return nullptr;
     }
 }
 
@@ -1062,6 +1097,27 @@ int launch_selftest_copy(const void* src, void* dst, int64_t n16, int lane_bytes
     void* args[] = {&src, &dst, &n16};
     const void* fn = vpl == 1 ? copy_fn<1>(group_waves) : vpl == 2 ? copy_fn<2>(group_waves)
                    : vpl == 4 ? copy_fn<4>(group_waves) : copy_fn<8>(group_waves);
+    return launch(fn, grid, dim3(64 * group_waves), args, stream);
+}
+
+template <int VPL, bool GATHER>
+static const void* stream_fn(int wpb) {
+    if (wpb == 1) return reinterpret_cast<const void*>(&selftest_stream_kernel<VPL, 1, GATHER>);
+    if (wpb == 2) return reinterpret_cast<const void*>(&selftest_stream_kernel<VPL, 2, GATHER>);
+    if (wpb == 4) return reinterpret_cast<const void*>(&selftest_stream_kernel<VPL, 4, GATHER>);
+    return reinterpret_cast<const void*>(&selftest_stream_kernel<VPL, 8, GATHER>);
+}
+
+template <bool GATHER>
+static const void* stream_fn(int vpl, int wpb) {
+    return vpl == 2 ? stream_fn<2, GATHER>(wpb) : vpl == 4 ? stream_fn<4, GATHER>(wpb) : stream_fn<8, GATHER>(wpb);
+}
+
+int launch_selftest_stream(const void* src, void* dst, int64_t tiles, int lane_elems, int group_waves, bool gather,
+                           void* stream) {
+    const dim3 grid((unsigned)((tiles + group_waves - 1) / group_waves));
+    void* args[] = {&src, &dst, &tiles};
+    const void* fn = gather ? stream_fn<true>(lane_elems, group_waves) : stream_fn<false>(lane_elems, group_waves);
     return launch(fn, grid, dim3(64 * group_waves), args, stream);
 }
 

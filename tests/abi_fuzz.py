@@ -52,7 +52,7 @@ def _shape(rng):
 def fuzz(lib, n=20000, seed=7):
     rng = np.random.default_rng(seed)
     for _ in range(n):
-        which = int(rng.integers(0, 10))
+        which = int(rng.integers(0, 12))
         if which == 0:
             rc = lib.kvq_fp16_to_fp8(_ptr(rng), _ptr(rng), _shape(rng), _size(rng), _size(rng), _size(rng), None)
         elif which == 1:
@@ -74,6 +74,17 @@ def fuzz(lib, n=20000, seed=7):
             rc = lib.kvq_bytes_per_token(int(rng.choice(FMT)), _size(rng), _size(rng))
             assert rc >= 0 or rc in CODES, rc
             continue
+        elif which == 10:
+            size = _int(rng) * int(rng.choice([1, 16, 1024]))
+            rc = lib.kvq_selftest_copy(_ptr(rng), _ptr(rng), size, int(rng.choice([0, 16, 32, 48, 64, 128, 256])),
+                                       int(rng.choice([0, 1, 2, 3, 4, 8, 16])), _int(rng), None)
+        elif which == 11:
+            light = _int(rng) * int(rng.choice([1, 16, 1024]))
+            k = int(rng.choice([1, 2, 3, 4, 8, 16]))
+            heavy = light * k if rng.random() < 0.8 else _int(rng) * 1024
+            src, dst = (heavy, light) if rng.random() < 0.5 else (light, heavy)
+            rc = lib.kvq_selftest_stream(_ptr(rng), src, _ptr(rng), dst, int(rng.choice([0, 1, 2, 3, 4, 8, 16])),
+                                         int(rng.choice([0, 1, 2, 4, 8, 16])), None)
         elif which == 8:
             f = lib.kvq_selftest_codes
             rc = f(_ptr(rng), _int(rng) * 8 if rng.random() < 0.5 else _int(rng), _ptr(rng), _int(rng),

@@ -52,6 +52,9 @@ int main(void)
           == KVQ_ERR_NULL);
     CHECK(kvq_selftest_fastdiv((const uint32_t*)p, 4, 0, (uint32_t*)q, NULL) == KVQ_ERR_RANGE);
     CHECK(kvq_selftest_scales((const uint16_t*)p, 4, 5, (uint16_t*)q, NULL) == KVQ_ERR_WBITS);
+    CHECK(kvq_selftest_copy(p, q, 1000, 16, 1, 0, NULL) == KVQ_ERR_RANGE);
+    CHECK(kvq_selftest_stream(p, 4096, q, 2048, 4, 1, NULL) == KVQ_ERR_RANGE);
+    CHECK(kvq_selftest_stream(p, 0, q, 0, 4, 1, NULL) == KVQ_OK);
 
     /* zero work validates and returns without a launch */
     CHECK(kvq_fp16_to_q_kv(p, q, (char*)q + (1 << 24), NULL, NULL, NULL, s, 0, 0, 4, 0, NULL, NULL, 0, 4, NULL)

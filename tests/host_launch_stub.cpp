@@ -54,5 +54,9 @@ int launch_selftest_copy(const void*, void*, int64_t n16, int, int, int64_t, voi
     if (n16 >= (INT64_C(1) << 32)) abort();
     return no_device();
 }
+int launch_selftest_stream(const void*, void*, int64_t tiles, int, int group_waves, bool, void*) {
+    if (mul_or_abort((tiles + group_waves - 1) / group_waves * group_waves, 64) >= (INT64_C(1) << 32)) abort();
+    return no_device();
+}
 
 }  // namespace kvq

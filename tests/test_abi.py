@@ -177,6 +177,31 @@ def test_selftest_copy_validation(lib):
     assert f(A, A + GB, 0, 16, 1, 0, None) == 0
 
 
+def test_selftest_stream_validation(lib):
+    """The uneven-traffic reference accepts only the two size ratios, whole
+    1024-byte tiles on the light side and the listed lane and group sizes,
+    and rejects everything else before any launch; zero sizes return
+    without one."""
+    f = lib.kvq_selftest_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    assert f(None, 4096, A + GB, 1024, 4, 1, None) == NULL
+    assert f(A, 4096, None, 1024, 4, 1, None) == NULL
+    for le in (0, 1, 3, 16):
+        assert f(A, 4096 * le, A + GB, 4096, le, 1, None) == RANGE
+    for gw in (0, 3, 16):
+        assert f(A, 4096, A + GB, 1024, 4, gw, None) == RANGE
+    assert f(A, 4096, A + GB, 2048, 4, 1, None) == RANGE          # neither ratio
+    assert f(A, 2048, A + GB, 512, 4, 1, None) == RANGE           # light side not whole tiles
+    assert f(A, -4096, A + GB, -1024, 4, 1, None) == RANGE
+    assert f(A, 1 << 56, A + GB, 1 << 54, 4, 1, None) == RANGE
+    assert f(A + 8, 4096, A + GB, 1024, 4, 1, None) == ALIGN
+    assert f(A, 4096, A + 2048, 1024, 4, 1, None) == OVERLAP       # gather
+    assert f(A, 1024, A + 512, 4096, 4, 1, None) == OVERLAP        # scatter
+    assert f(A, 0, A + GB, 0, 4, 1, None) == 0
+
+
 def test_size_bounds(lib):
     """Rows up to 2^20 elements are accepted, longer ones are SHAPE; a call
     whose work units exceed the 32-bit numbering is RANGE (checked before any

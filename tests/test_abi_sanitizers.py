@@ -21,7 +21,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # the host-side ABI tests that call into the library (not the ones that
 # inspect the built HIP library's file or compile other programs)
-HOST_TESTS = ("strerror_and_version or q_validation or selftest_fastdiv_validation or size_bounds or "
+HOST_TESTS = ("strerror_and_version or q_validation or selftest_fastdiv_validation or selftest_copy_validation or "
+              "selftest_stream_validation or size_bounds or "
               "zero_work or fp8_validation or count_match or binding_host_checks or per_tensor_validation or "
               "prefix_validation or bytes_per_token")
 

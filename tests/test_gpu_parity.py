@@ -650,3 +650,42 @@ def test_fp8_batch_beyond_grid_y(kvq):
     oracle.fp8_to_fp16(w8, wb, 70000, 1, 1)
     byte_diff(host(o8), w8, "8-bit, 70,000 sequences")
     byte_diff(host(ob), wb.view(np.uint16), "fp16 back, 70,000 sequences")
+
+
+# ---------------------------------------------------------------- bandwidth references
+@pytest.mark.parametrize("lane_bytes,group_waves,max_waves", [(16, 1, 0), (64, 4, 0), (128, 2, 0), (32, 8, 5)])
+def test_selftest_copy(kvq, lane_bytes, group_waves, max_waves):
+    """The plain copy moves every byte, for sizes that end inside a tile and
+    with waves striding over the tiles."""
+    t = torch()
+    n = 16 * (64 * 8 * 13 + 37)
+    src = t.randint(0, 256, (n,), dtype=t.uint8, device="cuda")
+    dst = t.zeros(n + 256, dtype=t.uint8, device="cuda")
+    kvq.kvq_selftest_copy(src, dst[:n], lane_bytes, group_waves, max_waves)
+    assert t.equal(dst[:n], src) and int(dst[n:].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("lane_elems", [2, 4, 8])
+@pytest.mark.parametrize("group_waves", [1, 4])
+def test_selftest_stream(kvq, lane_elems, group_waves):
+    """The uneven-traffic reference: gather writes the XOR of each lane's
+    heavy-side elements, scatter writes each light element lane_elems
+    times; nothing outside dst is written."""
+    t = torch()
+    tiles = 37
+    light = 1024 * tiles
+    heavy = light * lane_elems
+    src = t.randint(0, 256, (heavy,), dtype=t.uint8, device="cuda")
+    out = t.zeros(light + 1024, dtype=t.uint8, device="cuda")
+    kvq.kvq_selftest_stream(src, out[:light], lane_elems, group_waves)
+    s = host(src).view(np.uint32).reshape(tiles, lane_elems, 64, 4)
+    want = np.bitwise_xor.reduce(s, axis=1).reshape(-1)
+    got = host(out).view(np.uint32)
+    assert np.array_equal(got[:light // 4], want) and not got[light // 4:].any()
+    src2 = t.randint(0, 256, (light,), dtype=t.uint8, device="cuda")
+    out2 = t.zeros(heavy + 1024, dtype=t.uint8, device="cuda")
+    kvq.kvq_selftest_stream(src2, out2[:heavy], lane_elems, group_waves)
+    s2 = host(src2).view(np.uint32).reshape(tiles, 1, 64, 4)
+    got2 = host(out2).view(np.uint32)
+    want2 = np.broadcast_to(s2, (tiles, lane_elems, 64, 4)).reshape(-1)
+    assert np.array_equal(got2[:heavy // 4], want2) and not got2[heavy // 4:].any()
