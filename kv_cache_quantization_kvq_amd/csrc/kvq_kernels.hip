@@ -641,10 +641,14 @@ __device__ __forceinline__ void widen_run(const QLaunch& a, const GroupGeom& g, 
 #pragma unroll
                 for (int h = 0; h < NCH; ++h) q[p][j][h].s = ws[(p * NT + j) * 32 + h * 16 + (lane >> 2)];
     }
+    // Stores go tensor by tensor: the P rows of one tensor are adjacent in
+    // memory, so a wave writes one run per tensor rather than alternating
+    // K and V rows (paged Q8 10.03 against 10.18 us, 8-bit 9.71 against
+    // 10.07, per-layer Q4 8.68 against 8.97).
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
+    for (int j = 0; j < NT; ++j) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
+        for (int p = 0; p < P; ++p) {
             const int tensor = NT == 2 ? j : tsel;
             uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(tensor ? a.v_dst : a.k_dst) +
                                                   (rr[p] >= 0 ? rr[p] : 0) * R);
