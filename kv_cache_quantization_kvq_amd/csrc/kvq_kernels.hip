@@ -490,13 +490,24 @@ __device__ __forceinline__ void narrow_run(const QLaunch& a, const GroupGeom& g,
     }
 }
 
-// Every present tensor has format FMT.
+// FMT >= 0: every present tensor has format FMT; -1: per-tensor formats,
+// chosen per wave (a wave converts units of one tensor).
 template <int FMT, int MODE, int NU>
 __global__ __launch_bounds__(kThreads) void narrow_run_kernel(QLaunch a, GroupGeom g) {
     __shared__ uint4 lds[kWaves * (NU / 2)][kLdsSlots];
     int32_t b, tensor, k;
     const bool gok = decode_group(g, b, tensor, k);
-    narrow_run<FMT, MODE, NU>(a, g, lds + (threadIdx.x >> 6) * (NU / 2), gok, b, tensor, k);
+    uint4 (*wl)[kLdsSlots] = lds + (threadIdx.x >> 6) * (NU / 2);
+    if constexpr (FMT >= 0) {
+        narrow_run<FMT, MODE, NU>(a, g, wl, gok, b, tensor, k);
+    } else {
+        switch (tensor ? a.fmt_v : a.fmt_k) {   // wave-uniform
+            case 4: narrow_run<4, MODE, NU>(a, g, wl, gok, b, tensor, k); break;
+            case 6: narrow_run<6, MODE, NU>(a, g, wl, gok, b, tensor, k); break;
+            case 8: narrow_run<8, MODE, NU>(a, g, wl, gok, b, tensor, k); break;
+            default: narrow_run<0, MODE, NU>(a, g, wl, gok, b, tensor, k); break;
+        }
+    }
 }
 
 // ================================================================ compact -> fp16, runs of positions
@@ -909,7 +920,8 @@ static const void* narrow_run_fn(int fmt) {
         case 4: return reinterpret_cast<const void*>(&narrow_run_kernel<4, MODE, kNarrowUnits>);
         case 6: return reinterpret_cast<const void*>(&narrow_run_kernel<6, MODE, kNarrowUnits>);
         case 8: return reinterpret_cast<const void*>(&narrow_run_kernel<8, MODE, kNarrowUnits>);
-        default: return nullptr;   // no single format: the caller takes the one-unit kernel
+        case -1: return reinterpret_cast<const void*>(&narrow_run_kernel<-1, MODE, kNarrowUnits>);
+        default: return nullptr;
     }
 }
 
@@ -934,10 +946,10 @@ static int launch_to_compact(const QLaunch& a, void* stream) {
     const bool paged = a.page_size != 0;
     const int fmt = common_format(a);
     const int ntens = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
-    if (a.R % 1024 == 0 && fmt >= 0) {
-        // two units of one tensor per wave (one format for the launch; K
-        // and V at different widths measured faster one unit per wave: 18.5
-        // against 19.3 us for K-Q4 + V-Q6 at 64 x 256 positions)
+    if (a.R % 1024 == 0) {
+        // two units of one tensor per wave, also when K and V have
+        // different formats (the wave takes its tensor's: K-Q4 + V-Q6 at
+        // 64 x 256 positions 18.40 against 18.98 us one unit per wave)
         GroupGeom g;
         g.nseg = a.R / 1024;
         g.seg_div = make_fastdiv((uint32_t)g.nseg);

@@ -3,9 +3,10 @@ the CPU oracle, byte for byte (every output byte, untouched sentinel bytes
 included).
 
 The kernels pick their work decomposition per launch: rows whose length is
-a multiple of 1024 elements are quantized two row segments per wave through
-an LDS transpose (one 32-element block per lane), other rows one segment
-per wave; paged launches of 8,192 to 16,384 units are widened in runs of
+a multiple of 1024 elements are quantized two row segments of one tensor
+per wave through an LDS transpose (one 32-element block per lane; with K
+and V at different formats each wave takes its tensor's), other rows one
+segment per wave; paged launches of 8,192 to 16,384 units are widened in runs of
 4 positions of K and V (8 of one tensor) per wave with workgroups
 renumbered by XCD, other paged launches one position per wave; contiguous
 K + V launches up to 16,384 units in runs of 2 positions (up to 8,192
@@ -170,10 +171,14 @@ def test_long_rows(kvq, heads, fmt):
     _roundtrip(kvq, k, v, fmt, fmt, batch, 1, width, ps, sl, bt, what="paged R=%d fmt=%d" % (R, fmt))
 
 
-@pytest.mark.parametrize("fmts", [(4, 6), (6, 4), (0, 8), (8, 0)])
+MIXED = [(fk, fv) for fk in (4, 6, 8, 0) for fv in (4, 6, 8, 0) if fk != fv]
+
+
+@pytest.mark.parametrize("fmts", MIXED)
 def test_mixed_formats_run_size(kvq, fmts):
-    """K and V at different formats in one launch at the run size (one
-    tensor per wave, 8 positions, format chosen per wave)."""
+    """K and V at different formats in one launch at the run size: quantize
+    two units of one tensor per wave in that tensor's format, widen one
+    tensor per wave, 8 positions."""
     rng = np.random.default_rng(4300 + 10 * fmts[0] + fmts[1])
     batch, width, ps = 16, 300, 7
     cols = (width + 12) // ps + 2
@@ -182,6 +187,27 @@ def test_mixed_formats_run_size(kvq, fmts):
     k, v = _data(rng, shape, 1.0), _data(rng, shape, 1.0)
     sl, bt = _tables(rng, dim0, batch, cols, ps, width)
     _roundtrip(kvq, k, v, fmts[0], fmts[1], batch, 0, width, ps, sl, bt, what="mixed %s" % (fmts,))
+
+
+@pytest.mark.parametrize("heads", [8, 16, 24])
+@pytest.mark.parametrize("fmts", [(4, 6), (0, 8), (8, 4), (6, 0)])
+def test_mixed_formats_contig_and_long_rows(kvq, heads, fmts):
+    """K and V at different formats on contiguous windows, and paged with
+    rows of 1024, 2048 and 3072 elements (a pair of units spans two rows
+    when a row has an odd number of segments)."""
+    rng = np.random.default_rng(4350 + heads + 10 * fmts[0] + fmts[1])
+    shape = (6, 48, heads, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 3.0)
+    _log("mixed %s heads=%d contig" % (fmts, heads))
+    _roundtrip(kvq, k, v, fmts[0], fmts[1], 5, 3, 37, what="mixed contig %s heads=%d" % (fmts, heads))
+    batch, ps, width = 6, 5, 41
+    cols = (width + 12) // ps + 2
+    dim0 = batch * cols + 2
+    pshape = (dim0, ps, heads, 128)
+    k, v = _data(rng, pshape, 0.5), _data(rng, pshape, 2.0)
+    sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+    _log("mixed %s heads=%d paged" % (fmts, heads))
+    _roundtrip(kvq, k, v, fmts[0], fmts[1], batch, 1, width, ps, sl, bt, what="mixed paged %s heads=%d" % (fmts, heads))
 
 
 @pytest.mark.parametrize("which", ["k", "v"])
