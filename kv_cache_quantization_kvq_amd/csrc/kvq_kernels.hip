@@ -12,7 +12,8 @@
 //   page's calls, or (b, position p < max_len) for the full-prefix widen.
 //
 //   fp16 -> compact (quantize, 8-bit narrow), R % 1024 == 0: one wavefront
-//     per pair of units of one tensor.  The wave reads its 4 KB of fp16 with
+//     per pair of units of one tensor, in that tensor's format when K and
+//     V formats differ.  The wave reads its 4 KB of fp16 with
 //     contiguous 16-byte lanes, passes it through LDS, and lane L then owns
 //     32-element block L (unit L / 32): the absmax, scale and codes of a
 //     block are one lane's work.  Q4 codes (16 bytes per block) are stored
@@ -25,9 +26,9 @@
 //     wavefront per run of P consecutive positions of one sequence (P = 1,
 //     2, 4 or 8 by launch size), both tensors (or one tensor when K and V
 //     formats differ, or for large contiguous launches).  Every load of
-//     the wave is issued before its first store; lane l converts chunks
-//     (8 elements) l and l + 64 of each unit, so every 128-bit store of the
-//     wave is contiguous.
+//     the wave is issued before its first store, and the stores go tensor
+//     by tensor; lane l converts chunks (8 elements) l and l + 64 of each
+//     unit, so every 128-bit store of the wave is contiguous.
 //   The paged row of a position is resolved from scalar loads of
 //   cache_seqlens[b] and block_table[b][p / page_size], once per run.
 //
