@@ -990,10 +990,11 @@ static int launch_to_compact(const QLaunch& a, void* stream) {
 
 // ---------------------------------------------------------------- compact -> fp16
 //
-// Paged launches of 8,192 to 32,768 units run P = 4 positions with both
-// tensors, or P = 8 positions of one tensor, per wave (1,024 to 4,096
-// waves): a single resident generation whose waves each keep 8 units in
-// flight, so every lookup finishes before the chip's memory queues fill.
+// Paged launches of 8,192 to 32,768 units run P = 2, 4 or 8 positions
+// with both tensors (about 2,048 waves), or P = 8 positions of one tensor,
+// per wave: a single resident generation whose waves each keep several
+// units in flight, so every lookup finishes before the chip's memory
+// queues fill.
 // Other paged launches take one position per wave: small ones to fill the
 // chip, large ones because many short waves stream better over several
 // generations (both tensors of a position in one wave, sharing the lookup).
@@ -1016,7 +1017,7 @@ static const void* widen_fn(int P, int NT) {
     if (NT == 1 && P == 8) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 8, 1>);
     if (NT == 2 && P == 1) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 1, 2>);
     if (NT == 2 && P == 4) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 4, 2>);
-    if constexpr (MODE == kContig) {
+    if constexpr (MODE != kPrefix) {
         if (NT == 2 && P == 2) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 2, 2>);
         if (NT == 2 && P == 8) return reinterpret_cast<const void*>(&widen_run_kernel<FMT, MODE, NCH, GUARD, 8, 2>);
     }
@@ -1065,6 +1066,16 @@ static int launch_to_fp16(const QLaunch& a, int mode, void* stream) {
     // 19.3 us for K-Q4 + V-Q6 at 64 x 256 positions)
     const bool run = units >= 8192 && units <= (mode == kPaged && NT == 2 ? 32768 : 16384);
     int P = run ? (NT == 2 ? 4 : 8) : 1;
+    // paged K + V runs keep about 2,048 waves: 2 positions per wave below
+    // 12,288 units (16 x 256 positions: Q4 5.06 against 5.30 us, Q8 5.74
+    // against 6.02, 8-bit 5.41 against 5.74), 8 from 24,576 units for Q4
+    // and 8-bit (64 x 256 positions: 17.39 against 18.26 us, 8-bit 19.46
+    // against 20.10); Q6 and Q8 keep 4 there, where their 8-unit waves stage
+    // the scales (Q6 with 8 positions 19.40 against 18.95 us)
+    if (run && mode == kPaged && NT == 2) {
+        if (units < 12288) P = 2;
+        else if (units >= 24576 && (fmt == 4 || fmt == 0)) P = 8;
+    }
     // contiguous K + V launches up to 16,384 units: 2 positions per wave up
     // to 8,192 units, 8 above (4 x 512 positions: 3.35 against 4.09 us for
     // one position; 4 x 2,048 positions: 8.01 against 8.53 us for 4)

@@ -6,8 +6,8 @@ The kernels pick their work decomposition per launch: rows whose length is
 a multiple of 1024 elements are quantized two row segments of one tensor
 per wave through an LDS transpose (one 32-element block per lane; with K
 and V at different formats each wave takes its tensor's), other rows one
-segment per wave; paged launches of 8,192 to 16,384 units are widened in runs of
-4 positions of K and V (8 of one tensor) per wave with workgroups
+segment per wave; paged launches of 8,192 to 32,768 units are widened in runs
+of 2, 4 or 8 positions of K and V (8 of one tensor) per wave with workgroups
 renumbered by XCD, other paged launches one position per wave; contiguous
 K + V launches up to 16,384 units in runs of 2 positions (up to 8,192
 units) or 8.  These cases sit on each side
@@ -319,9 +319,10 @@ def test_block_absmax_every_magnitude(kvq, R):
 @pytest.mark.parametrize("fmt", [4, 6, 0])
 def test_paged_large_launches(kvq, batch, fmt):
     """Paged K + V launches past 16,384 units: 48 x 300 positions (28,800
-    units, still runs of 4 positions per wave) and 70 x 300 (42,000 units,
-    one position per wave), both with workgroups renumbered by XCD over a
-    grid padded to a multiple of 8; pages of 16 tokens, invalid entries."""
+    units, runs of 8 positions per wave for Q4 and 8-bit, 4 for Q6) and
+    70 x 300 (42,000 units, one position per wave), both with workgroups
+    renumbered by XCD over a grid padded to a multiple of 8; pages of 16
+    tokens, invalid entries."""
     rng = np.random.default_rng(4900 + batch + fmt)
     width, ps = 300, 16
     cols = (width + 12) // ps + 2
@@ -331,3 +332,23 @@ def test_paged_large_launches(kvq, batch, fmt):
     sl, bt = _tables(rng, dim0, batch, cols, ps, width)
     _log("paged large launch batch=%d fmt=%d" % (batch, fmt))
     _roundtrip(kvq, k, v, fmt, fmt, batch, 1, width, ps, sl, bt, what="paged large b=%d fmt=%d" % (batch, fmt))
+
+
+@pytest.mark.parametrize("batch", [16, 48])
+@pytest.mark.parametrize("fmt", [4, 6, 0])
+@pytest.mark.parametrize("heads", [4, 6])
+def test_paged_run_lengths_short_rows(kvq, heads, fmt, batch):
+    """Paged K + V launches with rows of 512 elements (one chunk per lane)
+    and 768 (a guarded partial segment): 16 x 260 positions (8,320 units,
+    runs of 2 positions) and 48 x 260 (24,960 units: runs of 8 for Q4 and
+    8-bit, 4 for Q6); pages of 16 tokens, invalid entries."""
+    rng = np.random.default_rng(5000 + 100 * heads + 10 * fmt + batch)
+    width, ps = 260, 16
+    cols = (width + 12) // ps + 2
+    dim0 = batch * cols + 3
+    shape = (dim0, ps, heads, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 0.5)
+    sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+    _log("paged run lengths R=%d fmt=%d batch=%d" % (heads * 128, fmt, batch))
+    _roundtrip(kvq, k, v, fmt, fmt, batch, 2, width, ps, sl, bt,
+               what="paged runs R=%d fmt=%d b=%d" % (heads * 128, fmt, batch))
