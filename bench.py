@@ -122,13 +122,15 @@ class PagedKV:
         self.dequant(d)
 
 
-def time_kernels(torch, launches, reps):
-    """Average device duration of each named launch: `reps` launches of that
-    kernel alone (rotating over its argument list) are captured in one HIP
-    graph, which is replayed between two events on the current stream.
-    Consecutive launches in a graph run back to back, so the average is the
-    kernel's own duration plus the (near-zero) dispatch gap; returns
-    {name: seconds}."""
+def time_kernels(torch, launches, reps, replays=9):
+    """Device duration per launch of each named launch: `reps` launches of
+    that kernel alone (rotating over its argument list) are captured in one
+    HIP graph; after two untimed replays (the first inputs touched, clocks
+    up after any host-side setup) the graph is replayed `replays` times,
+    each between two events on the current stream, and the median replay
+    time over `reps` is taken.  Consecutive launches in a graph run back to
+    back, so this is the kernel's own duration plus the (near-zero)
+    dispatch gap; returns {name: seconds}."""
     out = {}
     for name, fn, args in launches:
         side = torch.cuda.Stream()
@@ -142,14 +144,18 @@ def time_kernels(torch, launches, reps):
         with torch.cuda.graph(g):
             for i in range(reps):
                 fn(args[i % len(args)])
-        g.replay()
+        for _ in range(2):
+            g.replay()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        out[name] = a.elapsed_time(b) * 1e-3 / reps
+        times = []
+        for _ in range(replays):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3 / reps)
+        out[name] = float(np.median(times))
         del g
     return out
 
