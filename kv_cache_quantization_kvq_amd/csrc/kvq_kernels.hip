@@ -511,6 +511,65 @@ __global__ __launch_bounds__(kThreads) void narrow_run_kernel(QLaunch a, GroupGe
     }
 }
 
+// ================================================================ fp16 -> block codes, one unit per wave
+//
+// R % 1024 == 0, one common block format.  A wave converts one unit of one
+// (sequence, tensor).  Its two loads are whole 1 KB runs (lane l: chunks l
+// and 64 + l); an LDS pass hands lane l chunks 2l and 2l + 1 (16
+// consecutive elements), so a 32-element block is a lane pair (its maximum
+// one DPP exchange) and the lane's codes -- 8, 12 or 16 bytes -- are
+// contiguous with its neighbours': every code store is a whole run, with no
+// restaging.  Twice as many waves as the two-unit kernel, each with half the
+// work.
+template <int WBITS, int MODE>
+__global__ __launch_bounds__(kThreads) void quant_lanepair_kernel(QLaunch a, GroupGeom g) {
+    __shared__ uint4 lds[kWaves][128];
+    uint4* wl = lds[threadIdx.x >> 6];
+    int32_t b, tensor, k;
+    const bool gok = decode_group(g, b, tensor, k);
+    const int lane = threadIdx.x & 63;
+    const int32_t R = a.R;
+    const int32_t t = (int32_t)fast_div((uint32_t)k, g.seg_div);   // k < width * nseg: one unit per group
+    const int32_t seg = k - t * g.nseg;
+    const int32_t d[1] = {0};
+    const bool tin[1] = {true};
+    int64_t rr[1];
+    resolve_positions<MODE, 1>(a, g.page_div, b, t, d, tin, rr);
+    const bool live = gok && rr[0] >= 0;
+    const int64_t row = rr[0] >= 0 ? rr[0] : 0;   // a skipped unit reads row 0 and stores nothing
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(tensor ? a.v_src : a.k_src) +
+                                                      row * R + seg * 1024);
+    const uint4 x0 = ld_nt(src + lane);
+    const uint4 x1 = ld_nt(src + 64 + lane);
+    wl[lane] = x0;
+    wl[64 + lane] = x1;
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's own LDS writes are complete
+    __builtin_amdgcn_wave_barrier();
+    const uint4 v[2] = {wl[2 * lane], wl[2 * lane + 1]};
+    const uint32_t s16 = scale_from_absmax<WBITS>(pair_max(absmax_2chunks(v[0], v[1])));
+    const ScaleOps so = prep_scale(s16);
+    uint32_t u[2][8];
+    quant_chunks<WBITS, 2>(v, s16, so, u);
+    uint8_t* c = static_cast<uint8_t*>(tensor ? a.v_dst : a.k_dst) + row * (int64_t)(R / 8 * WBITS) +
+                 (int64_t)seg * (128 * WBITS);
+    if constexpr (WBITS == 4) {
+        if (live) st_nt(reinterpret_cast<uint2*>(c) + lane, make_uint2(pack_q4(u[0]), pack_q4(u[1])));
+    } else if constexpr (WBITS == 8) {
+        const uint4 q = make_uint4(pack_q8x4(u[0][0], u[0][1], u[0][2], u[0][3]), pack_q8x4(u[0][4], u[0][5], u[0][6], u[0][7]),
+                                   pack_q8x4(u[1][0], u[1][1], u[1][2], u[1][3]), pack_q8x4(u[1][4], u[1][5], u[1][6], u[1][7]));
+        if (live) st_nt(reinterpret_cast<uint4*>(c) + lane, q);
+    } else {
+        uint32_t lo0, hi0, lo1, hi1;
+        pack_q6(u[0], lo0, hi0);
+        pack_q6(u[1], lo1, hi1);
+        const uint32_t d1 = __builtin_amdgcn_perm(lo1, hi0, 0x05040100u);   // hi0.lo16 | lo1.lo16 << 16
+        const uint32_t d2 = __builtin_amdgcn_alignbit(hi1, lo1, 16);        // lo1 >> 16 | hi1 << 16
+        if (live) st_nt3(c + 12 * lane, lo0, d1, d2);
+    }
+    uint16_t* scales = static_cast<uint16_t*>(tensor ? a.v_scales : a.k_scales);
+    if (live && (lane & 1) == 0) st_nt(scales + row * (int64_t)(R >> 5) + seg * 32 + (lane >> 1), s16);
+}
+
 // ================================================================ compact -> fp16, runs of positions
 //
 // A group is (sequence b, block of P positions, segment) and NT tensors:
@@ -943,10 +1002,49 @@ static const void* unit_fn(int fmt, bool guard) {
                  : reinterpret_cast<const void*>(&narrow_unit_kernel<MODE, false>);
 }
 
+template <int MODE>
+static const void* lanepair_fn(int fmt) {
+    switch (fmt) {
+        case 4: return reinterpret_cast<const void*>(&quant_lanepair_kernel<4, MODE>);
+        case 6: return reinterpret_cast<const void*>(&quant_lanepair_kernel<6, MODE>);
+        case 8: return reinterpret_cast<const void*>(&quant_lanepair_kernel<8, MODE>);
+        default: return nullptr;
+    }
+}
+
+// One unit per wave (quant_lanepair_kernel) where it measured faster than
+// two (narrow_run_kernel): every paged Q6 / Q8 launch, whose two-unit waves
+// restage their codes through LDS (8 to 128 sequences x 256 positions: Q6
+// 3.92 / 6.28 / 10.49 / 18.61 / 33.79 against 4.50 / 6.44 / 10.63 / 19.02 /
+// 35.38 us, Q8 3.90 / 6.45 / 10.99 / 19.62 / 35.90 against 4.43 / 7.00 /
+// 11.32 / 20.35 / 38.18 us), and any block format up to 4,096 units, where
+// twice the waves fill more of the chip (paged Q4 at 8 x 256 positions 3.84
+// against 4.20 us, contiguous 4 x 512 positions 3.23 against 3.35 us).
+// Larger Q4 launches keep two units per wave (16 to 64 x 256 positions:
+// 5.77 / 9.85 / 17.39 against 5.59 / 9.43 / 16.99 us), and so do larger
+// contiguous ones (Q6 at 8 x 4,096 positions: 30.54 against 30.21 us).
+static bool use_lanepair(int fmt, bool paged, int64_t units) {
+    if (fmt != 4 && fmt != 6 && fmt != 8) return false;
+    return units <= 4096 || (paged && fmt != 4);
+}
+
 static int launch_to_compact(const QLaunch& a, void* stream) {
     const bool paged = a.page_size != 0;
     const int fmt = common_format(a);
     const int ntens = (a.k_src ? 1 : 0) + (a.v_src ? 1 : 0);
+    if (a.R % 1024 == 0 && use_lanepair(fmt, paged, (int64_t)a.batch * a.width * ntens * (a.R / 1024))) {
+        GroupGeom g;
+        g.nseg = a.R / 1024;
+        g.seg_div = make_fastdiv((uint32_t)g.nseg);
+        g.inner = (int32_t)((int64_t)a.width * g.nseg);   // one unit per group
+        g.inner_div = make_fastdiv((uint32_t)g.inner);
+        g.split = ntens == 2 ? 1 : 0;
+        g.tens0 = a.k_src ? 0 : 1;
+        g.n_groups = (int32_t)((int64_t)a.batch * ntens * g.inner);   // bounded by the host checks
+        g.page_div = make_fastdiv(paged ? (uint32_t)a.page_size : 1u);
+        const void* fn = paged ? lanepair_fn<kPaged>(fmt) : lanepair_fn<kContig>(fmt);
+        return launch_groups(fn, g, narrow_xcd(paged), a, stream);
+    }
     if (a.R % 1024 == 0) {
         // two units of one tensor per wave, also when K and V have
         // different formats (the wave takes its tensor's: K-Q4 + V-Q6 at

@@ -5,8 +5,9 @@ included).
 The kernels pick their work decomposition per launch: rows whose length is
 a multiple of 1024 elements are quantized two row segments of one tensor
 per wave through an LDS transpose (one 32-element block per lane; with K
-and V at different formats each wave takes its tensor's), other rows one
-segment per wave; paged launches of 8,192 to 32,768 units are widened in runs
+and V at different formats each wave takes its tensor's), or -- paged Q6 /
+Q8, and any block format up to 4,096 units -- one segment per wave with a
+lane pair per block; other rows one segment per wave; paged launches of 8,192 to 32,768 units are widened in runs
 of 2, 4 or 8 positions of K and V (8 of one tensor) per wave with workgroups
 renumbered by XCD, other paged launches one position per wave; contiguous
 K + V launches up to 16,384 units in runs of 2 positions (up to 8,192
@@ -171,6 +172,53 @@ def test_long_rows(kvq, heads, fmt):
     _roundtrip(kvq, k, v, fmt, fmt, batch, 1, width, ps, sl, bt, what="paged R=%d fmt=%d" % (R, fmt))
 
 
+@pytest.mark.parametrize("fmt", [4, 6, 8])
+@pytest.mark.parametrize("width", [1024, 1025])
+def test_contig_one_unit_quantize_threshold(kvq, fmt, width):
+    """Contiguous K + V at 4,096 units (one unit per quantize wave, lane-pair
+    blocks) and just above (two units per wave)."""
+    rng = np.random.default_rng(4700 + width + fmt)
+    shape = (3, 1100, 8, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 2.0)
+    _log("contig one-unit threshold width=%d fmt=%d" % (width, fmt))
+    _roundtrip(kvq, k, v, fmt, fmt, 2, 70, width, what="contig width=%d fmt=%d" % (width, fmt))
+
+
+@pytest.mark.parametrize("fmt", [4, 6, 8])
+@pytest.mark.parametrize("batch", [8, 9])
+def test_paged_one_unit_quantize(kvq, fmt, batch):
+    """Paged K + V at 4,096 units (8 x 256 positions: one unit per quantize
+    wave for every block format) and 4,608 (9 x 256: Q6 / Q8 still one unit
+    per wave, Q4 two), with pages of 7 tokens, invalid entries and positions
+    before the cache and past the table."""
+    rng = np.random.default_rng(4800 + 10 * batch + fmt)
+    width, ps = 256, 7
+    cols = (width + 12) // ps + 2
+    dim0 = batch * cols + 3
+    shape = (dim0, ps, 8, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 0.25)
+    sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+    _log("paged one-unit batch=%d fmt=%d" % (batch, fmt))
+    _roundtrip(kvq, k, v, fmt, fmt, batch, 0, width, ps, sl, bt, what="paged batch=%d fmt=%d" % (batch, fmt))
+
+
+@pytest.mark.parametrize("fmt", [6, 8])
+@pytest.mark.parametrize("which", ["K", "V"])
+def test_paged_one_unit_quantize_long_rows_one_tensor(kvq, fmt, which):
+    """Paged Q6 / Q8 with rows of 3072 elements (three segments per row, one
+    per wave) and one tensor only."""
+    rng = np.random.default_rng(5100 + fmt + (which == "V"))
+    heads, batch, width, ps = 24, 5, 61, 4
+    cols = (width + 12) // ps + 2
+    dim0 = batch * cols + 1
+    shape = (dim0, ps, heads, 128)
+    x = _data(rng, shape, 3.0)
+    sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+    k, v = (x, None) if which == "K" else (None, x)
+    _log("paged one-unit long rows %s fmt=%d" % (which, fmt))
+    _roundtrip(kvq, k, v, fmt, fmt, batch, 1, width, ps, sl, bt, what="paged %s R=3072 fmt=%d" % (which, fmt))
+
+
 MIXED = [(fk, fv) for fk in (4, 6, 8, 0) for fv in (4, 6, 8, 0) if fk != fv]
 
 
@@ -316,13 +364,14 @@ def test_block_absmax_every_magnitude(kvq, R):
 
 
 @pytest.mark.parametrize("batch", [48, 70])
-@pytest.mark.parametrize("fmt", [4, 6, 0])
+@pytest.mark.parametrize("fmt", [4, 6, 8, 0])
 def test_paged_large_launches(kvq, batch, fmt):
     """Paged K + V launches past 16,384 units: 48 x 300 positions (28,800
-    units, runs of 8 positions per wave for Q4 and 8-bit, 4 for Q6) and
-    70 x 300 (42,000 units, one position per wave), both with workgroups
-    renumbered by XCD over a grid padded to a multiple of 8; pages of 16
-    tokens, invalid entries."""
+    units, widened in runs of 8 positions per wave for Q4 and 8-bit, 4 for
+    Q6 and Q8) and 70 x 300 (42,000 units, one position per wave), both with
+    workgroups renumbered by XCD over a grid padded to a multiple of 8 (Q6
+    and Q8 quantized one unit per wave); pages of 16 tokens, invalid
+    entries."""
     rng = np.random.default_rng(4900 + batch + fmt)
     width, ps = 300, 16
     cols = (width + 12) // ps + 2
