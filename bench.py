@@ -545,7 +545,8 @@ def traffic_for(kernel, algo_bytes):
     if key not in kv:
         return None, "no figure for this kernel"
     return float(kv[key]), ("profiles/traffic_paged_q4.txt: rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch, "
-                            "each scaled by its reading for a 1 GiB copy (committed, same kernel sources)")
+                            "each scaled by its reading for the library's plain copy kernel (committed, taken on "
+                            "the same kernel sources)")
 
 
 def sources_digest():
