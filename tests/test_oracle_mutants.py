@@ -89,6 +89,18 @@ MUTANTS = [
      [("            return i;\n", "            return i + 1;\n", 1)]),
     ("count_match ignores max_a",
      [("int64_t n = max_a;", "int64_t n = len_a;", 1)]),
+    ("negative positions taken as position 0 instead of skipped",
+     [("if (p < 0) return -1;", "if (p < 0) p = 0;", 1)]),
+    ("codes multiply by a rounded reciprocal of the scale",
+     [("float v = xf / sf;", "float v = xf * (1.0f / sf);", 1)]),
+    ("codes not clamped",
+     [("            if (r < (float)(-Z)) r = (float)(-Z);\n", "", 1),
+      ("            if (r > (float)(Z - 1)) r = (float)(Z - 1);\n", "", 1)]),
+    ("pieces of a long row packed at the row start (pack and unpack agree)",
+     [("orc_pack_bits(u, len, wbits, crow + (int64_t)base * wbits / 8);", "orc_pack_bits(u, len, wbits, crow);", 1),
+      ("orc_unpack_bits(crow + (int64_t)base * wbits / 8, len, wbits, u);", "orc_unpack_bits(crow, len, wbits, u);", 1)]),
+    ("8-bit narrowing rounds to nearest instead of truncating",
+     [("{ return (uint8_t)(h >> 8); }", "{ return (uint8_t)((h + 0x80u) >> 8); }", 1)]),
     ("bytes per token without the scales",
      [("return orc_fmt_row_bytes(R, fmt) + 2 * orc_fmt_scale_count(R, fmt);",
        "return orc_fmt_row_bytes(R, fmt);", 1)]),
