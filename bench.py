@@ -396,6 +396,7 @@ def main():
                                          "dequant": round(td_total / args.steps * 1e6, 3)}}
     # counter cross-check: HBM bytes the counters saw per launch over the same duration
     roofline["counter_GBps"] = round(traffic / kt[dom] / 1e9, 1) if traffic is not None else None
+    roofline["rocprof"] = rocprof_check(roofline["avg_us"])
 
     def rows_fn(t, rows):
         idx = torch.from_numpy(np.asarray(rows, np.int64)).cuda()
@@ -526,19 +527,45 @@ def copy_floor(torch, kvq, launch_bytes):
     return out
 
 
-def traffic_for(kernel, algo_bytes):
-    """HBM bytes per launch from the committed counter summary and a label of
-    where they come from, or (None, reason) when the summary was taken on
-    other kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic_paged_q4.txt")
+def read_profile_keys(name):
+    """key = value lines of a committed profile summary, or None if absent."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
-        return None, "no counter summary"
+        return None
     kv = {}
     with open(path) as fh:
         for line in fh:
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
+    return kv
+
+
+def rocprof_check(avg_us):
+    """This run's per-launch event times against the per-dispatch means of
+    the committed rocprofv3 trace of the same command, when that trace was
+    taken on the same kernel sources."""
+    name = "paged_q4_kernel_trace.txt"
+    kv = read_profile_keys(name)
+    if kv is None:
+        return {"source": None, "reason": "no trace summary"}
+    if kv.get("sources_sha256") != sources_digest():
+        return {"source": "profiles/" + name, "reason": "taken on other kernel sources"}
+    out = {"source": "profiles/" + name, "trace_mean_us": {}, "event_vs_trace": {}}
+    for k in ("quant", "dequant"):
+        tr = float(kv["%s_trace_mean_ns" % k]) / 1000.0
+        out["trace_mean_us"][k] = round(tr, 3)
+        out["event_vs_trace"][k] = "%+.1f%%" % ((avg_us[k] / tr - 1.0) * 100.0)
+    return out
+
+
+def traffic_for(kernel, algo_bytes):
+    """HBM bytes per launch from the committed counter summary and a label of
+    where they come from, or (None, reason) when the summary was taken on
+    other kernel sources."""
+    kv = read_profile_keys("traffic_paged_q4.txt")
+    if kv is None:
+        return None, "no counter summary"
     if kv.get("sources_sha256") != sources_digest():
         return None, "profiles/traffic_paged_q4.txt was taken on other kernel sources"
     key = "%s_traffic_bytes_per_launch" % kernel
