@@ -345,22 +345,26 @@ def _absmax_blocks(rng):
     return np.concatenate([blocks, neg_zero, mixed_zero]).view(np.float16)
 
 
-@pytest.mark.parametrize("R", [1024, 1056])
-def test_block_absmax_every_magnitude(kvq, R):
+@pytest.mark.parametrize("R,copies", [(1024, 1), (1024, 5), (1056, 1)])
+def test_block_absmax_every_magnitude(kvq, R, copies):
     """The block maximum of |x| (scale and codes) for every finite fp16
     magnitude as the block's largest element, either sign, plus blocks of
-    negative and mixed zeros, through the two-unit kernel (rows of 1024)
-    and the one-unit kernel (rows of 1056, guarded), Q4 / Q6 / Q8."""
+    negative and mixed zeros, Q4 / Q6 / Q8, through each quantize kernel:
+    rows of 1024 in one launch of about 1,000 units (one unit per wave,
+    lane-pair blocks) and, the block set repeated 5 times, of about 5,000
+    units (two units per wave, block per lane), and rows of 1056 (one unit
+    per wave, guarded partial segment)."""
     rng = np.random.default_rng(4800 + R)
-    blocks = _absmax_blocks(rng)
+    blocks = np.tile(_absmax_blocks(rng), (copies, 1))
     per_row = R // 32
     rows = -(-blocks.shape[0] // per_row)
+    assert (rows > 4096) == (copies > 1)   # the launch rule's threshold between the two R = 1024 kernels
     flat = np.zeros((rows * per_row, 32), np.float16)
     flat[:blocks.shape[0]] = blocks
     x = flat.reshape(1, rows, R // 32, 32)
     for fmt in (4, 6, 8):
-        _log("block absmax R=%d fmt=%d" % (R, fmt))
-        _roundtrip(kvq, x, None, fmt, fmt, 1, 0, rows, what="absmax R=%d Q%d" % (R, fmt))
+        _log("block absmax R=%d copies=%d fmt=%d" % (R, copies, fmt))
+        _roundtrip(kvq, x, None, fmt, fmt, 1, 0, rows, what="absmax R=%d x%d Q%d" % (R, copies, fmt))
 
 
 @pytest.mark.parametrize("batch", [48, 70])
