@@ -151,16 +151,24 @@ def test_paged_single_width_run_size(kvq):
 @pytest.mark.parametrize("fmt", [4, 6, 8, 0])
 def test_long_rows(kvq, heads, fmt):
     """Rows of 2048 and 3072 elements (two or three segments: a pair of
-    units spans two rows when the count is odd), contiguous and paged, at a
-    small size and at the run size."""
+    units spans two rows when the count is odd): contiguous at a small size
+    (one unit per quantize wave) and past 4,096 units (two units per wave),
+    and paged at the run size."""
     rng = np.random.default_rng(4200 + heads + fmt)
     R = heads * 128
+    nseg = R // 1024
     shape = (6, 48, heads, 128)
     k, v = _data(rng, shape, 1.0), _data(rng, shape, 4.0)
     _log("long rows R=%d fmt=%d contig" % (R, fmt))
     _roundtrip(kvq, k, v, fmt, fmt, 5, 3, 37, what="contig R=%d fmt=%d" % (R, fmt))
+    # contiguous past the 4,096-unit threshold of the one-unit quantize waves
+    width = 4096 // (2 * nseg * 5) + 7
+    assert 5 * width * 2 * nseg > 4096
+    shape = (6, width + 9, heads, 128)
+    k, v = _data(rng, shape, 1.0), _data(rng, shape, 0.25)
+    _log("long rows R=%d fmt=%d contig, %d units" % (R, fmt, 5 * width * 2 * nseg))
+    _roundtrip(kvq, k, v, fmt, fmt, 5, 4, width, what="contig large R=%d fmt=%d" % (R, fmt))
     # paged at the run size: units = batch * width * 2 * nseg in [8192, 16384]
-    nseg = R // 1024
     batch, ps = 8, 5
     width = 8192 // (2 * nseg * batch) + 3
     cols = (width + 12) // ps + 2
@@ -405,3 +413,54 @@ def test_paged_run_lengths_short_rows(kvq, heads, fmt, batch):
     _log("paged run lengths R=%d fmt=%d batch=%d" % (heads * 128, fmt, batch))
     _roundtrip(kvq, k, v, fmt, fmt, batch, 2, width, ps, sl, bt,
                what="paged runs R=%d fmt=%d b=%d" % (heads * 128, fmt, batch))
+
+
+# ---------------------------------------------------------------- randomized run sizes
+_RUN_ROWS = ((8, 128), (16, 64), (4, 256), (16, 128), (24, 128))   # R = 1024, 1024, 1024, 2048, 3072
+_FMTS = (4, 6, 8, 0)
+
+
+def _random_run_case(rng):
+    """One seeded configuration at run sizes: rows of 1024 to 3072 elements,
+    2,000 to 14,000 units (both sides of the 4,096-unit one-unit quantize
+    threshold and of the 8,192-unit widen runs), contiguous or paged (page
+    sizes 1 to 64, invalid table entries, positions before the cache and
+    past the table), one format or two, both tensors or one."""
+    heads, head_dim = _RUN_ROWS[int(rng.integers(0, len(_RUN_ROWS)))]
+    nseg = heads * head_dim // 1024
+    present = ("kv", "k", "v")[int(rng.choice(3, p=[0.7, 0.15, 0.15]))]
+    ntens = 2 if present == "kv" else 1
+    fk = int(rng.choice(_FMTS))
+    fv = fk if rng.random() < 0.6 else int(rng.choice(_FMTS))
+    units = int(rng.integers(2000, 14001))
+    rows = max(1, units // (ntens * nseg))
+    batch = int(rng.integers(1, 65))
+    width = max(1, rows // batch)
+    c = {"present": present, "fk": fk, "fv": fv, "batch": batch, "width": width}
+    if rng.random() < 0.4:
+        offset = int(rng.integers(0, 6))
+        c.update(ps=0, sl=None, bt=None, offset=offset,
+                 shape=(batch + int(rng.integers(0, 3)), width + offset + int(rng.integers(0, 4)), heads, head_dim))
+    else:
+        ps = int(rng.choice([1, 3, 16, 64]))
+        cols = -(-(width + 16) // ps) + 1
+        dim0 = batch * cols + int(rng.integers(0, 5))
+        sl, bt = _tables(rng, dim0, batch, cols, ps, width)
+        c.update(ps=ps, sl=sl, bt=bt, offset=int(rng.integers(0, 4)), shape=(dim0, ps, heads, head_dim))
+    return c
+
+
+def test_randomized_run_sizes(kvq):
+    """40 seeded configurations at run sizes through the per-tensor entry
+    points (one common format takes the same kernels as the one-width
+    calls), both directions, against the oracle on every byte."""
+    rng = np.random.default_rng(20261205)
+    for case in range(40):
+        c = _random_run_case(rng)
+        k = _data(rng, c["shape"], 1.0) if "k" in c["present"] else None
+        v = _data(rng, c["shape"], 0.2) if "v" in c["present"] else None
+        what = "run case %d: %s %s fmts (%d,%d) batch %d width %d ps %d" % (
+            case, c["present"], c["shape"], c["fk"], c["fv"], c["batch"], c["width"], c["ps"])
+        _log(what)
+        _roundtrip(kvq, k, v, c["fk"], c["fv"], c["batch"], c["offset"], c["width"], c["ps"], c["sl"], c["bt"],
+                   what=what)
