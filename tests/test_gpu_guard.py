@@ -2,8 +2,9 @@
 a larger allocation with 256 sentinel bytes on both sides, and after the
 call the guard bytes must be unchanged.  The shapes exercise the guarded
 kernels (row segments shorter than a full wave, chunk tails), the 12-byte
-Q6 stores and the 8-bit chunk tails; windows and tables reach the first
-and last rows of each buffer.  Outputs are also compared with the oracle.
+Q6 stores and the 8-bit chunk tails, and the run kernels of rows of 1024
+and 3072 elements (one- and two-unit quantize waves, runs of positions);
+windows and tables reach the first and last rows of each buffer.  Outputs are also compared with the oracle.
 (Operations: ExLlamaV2 cache page, Description / I/O Contract: outputs are
 written in place on the touched rows only.)
 
@@ -55,6 +56,10 @@ def _ss(shape):
 
 
 SHAPES = [(2, 5, 3, 96), (1, 3, 5, 1376), (2, 2, 1, 32)]
+# rows of 1024 and 3072 elements (the run kernels): 20 units (one unit per
+# quantize wave), 4,206 units (two per wave, an odd count per sequence) and
+# 8,400 units (two per wave, three segments per row)
+RUN_SHAPES = [(2, 5, 8, 128), (3, 701, 8, 128), (2, 700, 24, 128)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -77,7 +82,7 @@ def test_guard_fp8_contig(kvq, shape):
         g.check("fp8 %s %s" % (shape, n))
 
 
-@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("shape", SHAPES + RUN_SHAPES)
 @pytest.mark.parametrize("wbits", [4, 6, 8])
 def test_guard_q_contig(kvq, shape, wbits):
     t = torch()
@@ -99,6 +104,8 @@ def test_guard_q_contig(kvq, shape, wbits):
     oracle.fp16_to_q_kv(k, okq, oks, v, ovq, ovs, batch, offset, width, 0, None, None, wbits)
     oracle.q_to_fp16_kv(okq, oko, oks, ovq, ovo, ovs, batch, offset, width, 0, None, None, wbits)
     byte_diff(host(gkq.tensor), okq, "K codes")
+    byte_diff(host(gvq.tensor), ovq, "V codes")
+    byte_diff(host(gks.tensor), oks.view(np.uint16), "K scales")
     byte_diff(host(gvs.tensor), ovs.view(np.uint16), "V scales")
     byte_diff(host(gko.tensor), oko.view(np.uint16), "K out")
     byte_diff(host(gvo.tensor), ovo.view(np.uint16), "V out")
@@ -156,6 +163,47 @@ def test_guard_per_tensor_paged_and_prefix(kvq, fmts, head_dim):
                  (gpo, "K prefix"), (gpv, "V prefix")):
         if g is not None:
             g.check("per-tensor %s %s %s" % (fmts, head_dim, n))
+
+
+@pytest.mark.parametrize("wbits", [4, 6, 8])
+def test_guard_paged_run_size(kvq, wbits):
+    """9 sequences x 256 positions of K and V in pages of 16 tokens (4,608
+    units: two units per Q4 quantize wave, one for Q6 / Q8; one position
+    per dequantize wave), the tables holding the first and the last
+    physical page: no byte outside any buffer is written."""
+    t = torch()
+    rng = np.random.default_rng(7700 + wbits)
+    B, width, ps = 9, 256, 16
+    cols = width // ps + 1
+    num_pages = B * cols
+    shape = (num_pages, ps, 8, 128)
+    bt = rng.permutation(num_pages).astype(np.int32).reshape(B, cols)
+    for want, at in ((num_pages - 1, (0, 0)), (0, (B - 1, cols - 2))):   # both live (positions < 256)
+        w = np.argwhere(bt == want)[0]
+        bt[tuple(w)], bt[at] = bt[at], want
+    sl = np.zeros(B, np.int32)
+    k = rng.standard_normal(shape).astype(np.float16)
+    v = (rng.standard_normal(shape) * 0.5).astype(np.float16)
+    gsl, gbt = Guarded(sl.shape, t.int32, sl), Guarded(bt.shape, t.int32, bt)
+    gk, gv = Guarded(shape, t.float16, k), Guarded(shape, t.float16, v)
+    gkq, gvq = Guarded(_cs(shape, wbits), t.uint8), Guarded(_cs(shape, wbits), t.uint8)
+    gks, gvs = Guarded(_ss(shape), t.float16), Guarded(_ss(shape), t.float16)
+    gko, gvo = Guarded(shape, t.float16), Guarded(shape, t.float16)
+    a = (B, 0, width, ps, gsl.tensor, gbt.tensor)
+    kvq.kvq_fp16_to_q_kv(gk.tensor, gkq.tensor, gks.tensor, gv.tensor, gvq.tensor, gvs.tensor, *a, wbits=wbits)
+    kvq.kvq_q_to_fp16_kv(gkq.tensor, gko.tensor, gks.tensor, gvq.tensor, gvo.tensor, gvs.tensor, *a, wbits=wbits)
+    okq, ovq = sentinel_np(_cs(shape, wbits), np.uint8), sentinel_np(_cs(shape, wbits), np.uint8)
+    oks, ovs = sentinel_np(_ss(shape), np.float16), sentinel_np(_ss(shape), np.float16)
+    oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
+    oracle.fp16_to_q_kv(k, okq, oks, v, ovq, ovs, B, 0, width, ps, sl, bt, wbits)
+    oracle.q_to_fp16_kv(okq, oko, oks, ovq, ovo, ovs, B, 0, width, ps, sl, bt, wbits)
+    for got, want, name in ((gkq, okq, "K codes"), (gvq, ovq, "V codes"), (gks, oks.view(np.uint16), "K scales"),
+                            (gvs, ovs.view(np.uint16), "V scales"), (gko, oko.view(np.uint16), "K out"),
+                            (gvo, ovo.view(np.uint16), "V out")):
+        byte_diff(host(got.tensor), want, "paged run Q%d %s" % (wbits, name))
+    for g, n in ((gsl, "cache_seqlens"), (gbt, "block_table"), (gk, "K in"), (gv, "V in"), (gkq, "K codes"),
+                 (gvq, "V codes"), (gks, "K scales"), (gvs, "V scales"), (gko, "K out"), (gvo, "V out")):
+        g.check("paged run Q%d %s" % (wbits, n))
 
 
 class Offset:
