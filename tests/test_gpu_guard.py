@@ -232,21 +232,22 @@ def test_sixteen_byte_aligned_buffers(kvq, off, wbits, paged):
     48 bytes past) a 256-byte boundary: the scalar whole-segment scale fetch
     of the Q4 / Q8 dequantize and every vector access must still read and
     write exactly the oracle's bytes.  Rows of 1024 elements (whole segments)
-    and of 2048."""
+    and of 2048 in small launches, and rows of 1024 in launches of about
+    9,000 units (two-unit quantize waves, runs of positions)."""
     t = torch()
-    for head_dim in (128, 256):
-        rng = np.random.default_rng(off + wbits + head_dim + (7 if paged else 0))
+    for head_dim, large in ((128, False), (256, False), (128, True)):
+        rng = np.random.default_rng(off + wbits + head_dim + (7 if paged else 0) + (100 if large else 0))
         if paged:
-            num_pages, ps, B, cols = 9, 4, 3, 3
+            num_pages, ps, B, cols = (291, 16, 17, 17) if large else (9, 4, 3, 3)
             shape = (num_pages, ps, 8, head_dim)
             bt = rng.permutation(num_pages).astype(np.int32)[:B * cols].reshape(B, cols)
-            sl = np.array([0, 3, 5], np.int32)
-            batch, offset, width = B, 0, 7
+            sl = np.arange(B, dtype=np.int32) % 5 if large else np.array([0, 3, 5], np.int32)
+            batch, offset, width = B, 0, (256 if large else 7)
             tabs = (ps, Offset(sl.shape, t.int32, off, sl).tensor, Offset(bt.shape, t.int32, off, bt).tensor)
             ref_tabs = (ps, sl, bt)
         else:
-            shape = (3, 10, 8, head_dim)
-            batch, offset, width = 2, 3, 6
+            shape = (3, 1500, 8, head_dim) if large else (3, 10, 8, head_dim)
+            batch, offset, width = (3, 5, 1490) if large else (2, 3, 6)
             tabs = (0, None, None)
             ref_tabs = (0, None, None)
         k = (rng.standard_normal(shape) * 2).astype(np.float16)
@@ -264,7 +265,8 @@ def test_sixteen_byte_aligned_buffers(kvq, off, wbits, paged):
         oko, ovo = sentinel_np(shape, np.float16), sentinel_np(shape, np.float16)
         oracle.fp16_to_q_kv(k, okq, oks, v, ovq, ovs, batch, offset, width, *ref_tabs, wbits)
         oracle.q_to_fp16_kv(okq, oko, oks, ovq, ovo, ovs, batch, offset, width, *ref_tabs, wbits)
-        what = "off %d Q%d %s head_dim %d" % (off, wbits, "paged" if paged else "contiguous", head_dim)
+        what = "off %d Q%d %s head_dim %d%s" % (off, wbits, "paged" if paged else "contiguous", head_dim,
+                                                 " large" if large else "")
         byte_diff(host(gkq.tensor), okq, what + " K codes")
         byte_diff(host(gvq.tensor), ovq, what + " V codes")
         byte_diff(host(gks.tensor), oks.view(np.uint16), what + " K scales")
