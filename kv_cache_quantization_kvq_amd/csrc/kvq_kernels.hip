@@ -19,7 +19,11 @@
 //     block are one lane's work.  Q4 codes (16 bytes per block) are stored
 //     straight from the lane; Q6 / Q8 codes are restaged through LDS so
 //     every store is 16 contiguous bytes per lane.  8-bit narrowing needs no
-//     transpose.
+//     transpose.  Every paged Q6 / Q8 launch, and any launch of one block
+//     format up to 4,096 units, instead takes one wavefront per unit: two
+//     whole 1 KB loads, an LDS pass that hands lane l elements 16 l ..
+//     16 l + 15, a block per lane pair, codes stored straight from each
+//     lane (8, 12 or 16 contiguous bytes).
 //   fp16 -> compact, other R: one wavefront per unit, lane l holding 16
 //     consecutive elements (a block is a lane pair).
 //   compact -> fp16 (dequantize, 8-bit widen, full-prefix widen): one
